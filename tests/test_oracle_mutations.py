@@ -1,0 +1,84 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one (CPU only).
+
+Each mutation is a textual edit of the oracle's source; the edited copy is
+executed as a throw-away module and run through the pin checks.  A mutation
+survives only if every check passes on it, which would mean the pins do not
+constrain that part of the oracle.
+"""
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "paged_attention.py")
+
+# (id, text to find, replacement, which occurrence (None = the only one))
+MUTATIONS = [
+    ("decode-gqa-modulo", "g = h // group", "g = h % num_kv_heads", 0),
+    ("prefill-gqa-modulo", "g = h // group", "g = h % num_kv_heads", 1),
+    ("decode-drops-scale", "scores = scale * (keys[:, g, :] @ q_vec)",
+     "scores = (keys[:, g, :] @ q_vec)", None),
+    ("prefill-drops-scale", "S = scale * (qh @ keys[:, g, :].T)", "S = (qh @ keys[:, g, :].T)",
+     None),
+    ("causal-top-left", "visible = cols <= (lk - lq) + rows", "visible = cols <= rows", None),
+    ("causal-off-by-one", "visible = cols <= (lk - lq) + rows",
+     "visible = cols < (lk - lq) + rows", None),
+    ("causal-unmasked", "S = np.where(visible, S, -np.inf)", "S = S", None),
+    ("gather-ignores-table", "return pool[table_row[pos // bs], pos % bs]",
+     "return pool[pos // bs, pos % bs]", None),
+    ("gather-swapped-index", "return pool[table_row[pos // bs], pos % bs]",
+     "return pool[table_row[pos % bs], pos // bs]", None),
+    ("softmax-sign", "p = np.exp(scores - m)", "p = np.exp(m - scores)", None),
+    ("decode-reads-keys-as-values", "out[b, h] = (p @ values[:, g, :]) / p.sum()",
+     "out[b, h] = (p @ keys[:, g, :]) / p.sum()", None),
+    ("decode-unnormalised", "out[b, h] = (p @ values[:, g, :]) / p.sum()",
+     "out[b, h] = (p @ values[:, g, :])", None),
+    ("prefill-max-wrong-axis", "m = S.max(axis=1, keepdims=True)",
+     "m = S.max(axis=0, keepdims=True)", None),
+    ("prefill-global-sum", "/ P.sum(axis=1, keepdims=True)", "/ P.sum()", None),
+    ("prefill-reads-keys-as-values", "(P @ values[:, g, :])", "(P @ keys[:, g, :])", None),
+    ("decode-drops-new-token", "L = int(context_lens[b])", "L = int(context_lens[b]) - 1", None),
+    ("prefill-wrong-query-head", "qh = widen(q[q0:q1, h, :], dtype)",
+     "qh = widen(q[q0:q1, g, :], dtype)", None),
+    ("store-swapped-index", "kc[s // bs, s % bs] = k[t]", "kc[s % bs, s // bs] = k[t]", None),
+    ("store-v-gets-k", "vc[s // bs, s % bs] = v[t]", "vc[s // bs, s % bs] = k[t]", None),
+    ("store-drops-slot-zero", "if s < 0:", "if s <= 0:", None),
+    ("store-writes-padding", "if s < 0:\n            continue", "if False:\n            continue",
+     None),
+    ("bf16-widen-shift", "<< 16", "<< 15", None),
+    ("prefill-key-length-from-q", "lk = int(cu_seqlens_k[b + 1]) - int(cu_seqlens_k[b])",
+     "lk = int(cu_seqlens_q[b + 1]) - int(cu_seqlens_q[b])", None),
+]
+
+
+def _mutant(find, repl, occurrence):
+    with open(ORACLE_SRC) as f:
+        src = f.read()
+    n = src.count(find)
+    if occurrence is None:
+        assert n == 1, f"pattern must occur once, found {n}: {find!r}"
+        src = src.replace(find, repl)
+    else:
+        assert n > occurrence, f"pattern occurs {n} times: {find!r}"
+        at = -1
+        for _ in range(occurrence + 1):
+            at = src.index(find, at + 1)
+        src = src[:at] + repl + src[at + len(find):]
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "<oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("mid,find,repl,occ", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(mid, find, repl, occ):
+    mod = _mutant(find, repl, occ)
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:          # an assertion or a crash: the mistake is caught
+            return
+    pytest.fail(f"mutation {mid!r} passed every pin")
