@@ -1,0 +1,153 @@
+/*
+ * pa.h -- C ABI of libpa: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * Three calls form one attention step of an LLM engine that keeps K/V in a
+ * block pool ("nano-vLLM Part 4: Whole-Engine Data Flow, Benchmarks, and the
+ * Gap to vLLM V1", section 3, prefill/decode table; "mini-vLLM", project
+ * summary):
+ *
+ *   pa_store_kv        write the new tokens' K/V rows into their pool slots;
+ *   pa_decode          one query token per sequence attends to its cached
+ *                      history, read through the sequence's block table;
+ *   pa_prefill_varlen  packed prompts (boundaries in cu_seqlens) attend
+ *                      causally; with cu_seqlens_k > cu_seqlens_q the extra
+ *                      keys are a cached prefix (prefix-cache hit).
+ *
+ * Data model, shared by every call:
+ *   K pool, V pool   [num_blocks, block_size, num_kv_heads, head_dim], row-major,
+ *                    two separate allocations of the same dtype;
+ *   block_tables     int32 [num_seqs, max_blocks_per_seq], row-major: physical
+ *                    block IDs of each sequence in logical order ("nano-vLLM
+ *                    Part 4", section 2: a table holds IDs, not K/V);
+ *   logical token j of sequence b lives at block block_tables[b][j / block_size],
+ *   offset j % block_size; its slot is that block * block_size + offset.
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing and keeps no pointer after it returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Return values report argument validation and launch
+ *     errors only; kernel results are ready when the stream is.
+ *   - dtype: PA_DTYPE_F32 (0) or PA_DTYPE_BF16 (1).  q, k, v, both pools and
+ *     out share it; accumulation is fp32; outputs are rounded to dtype with
+ *     round-to-nearest-even.
+ *   - Host integers (max_context_len, max_seqlen_q/k, total_q) size the launch
+ *     grid, so no device-to-host copy is needed.
+ *   - Device-resident preconditions are not checked on the device:
+ *     slots < num_blocks * block_size and distinct; block IDs in
+ *     [0, num_blocks); 1 <= context_lens[b] <= max_context_len;
+ *     cu_seqlens_* start at 0 and are non-decreasing; 0 <= Lq <= Lk per
+ *     sequence.  Kernels clamp block IDs and lengths so that a violated
+ *     precondition never reads or writes outside the caller's buffers; the
+ *     result is then unspecified.  With the environment variable PA_CHECK=1
+ *     the library copies the index arrays to the host, validates them and
+ *     returns PA_E_INVAL on a violation (this synchronises the stream).
+ *   - Outputs must not alias inputs; k/v must not alias the pools.
+ *   - The library is stateless; calls on different streams may overlap.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_E_INVAL = -1,        /* null pointer, bad size, Hq % Hkv != 0, bad index data */
+  PA_E_UNSUPPORTED = -2,  /* head_dim or dtype outside what the kernels cover */
+  PA_E_WORKSPACE = -3,    /* decode workspace too small */
+  PA_E_HIP = -4           /* HIP runtime error while launching */
+};
+
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/*
+ * Store: for each token t in [0, num_tokens) with s = slot_mapping[t] >= 0,
+ * copy row k[t] (num_kv_heads * head_dim elements) to k_cache slot s, i.e.
+ * element [s / block_size][s % block_size][:][:], and v[t] to v_cache slot s.
+ * A negative slot means "skip this row" (padding).  Rows are copied bit for
+ * bit.  Any head_dim >= 1 is accepted.
+ *   k, v          [num_tokens, num_kv_heads, head_dim], contiguous
+ *   k_cache, v_cache  the pools (modified in place)
+ *   slot_mapping  int32 [num_tokens]
+ * ("nano-vLLM Part 4", section 3: K/V is written for every new prompt token in
+ * prefill and for one token per sequence in decode; the smzdm Nano-vLLM
+ * walk-through, model implementation details: the store puts K and V at their
+ * physical position.)  num_tokens == 0 is a no-op (pointers may be NULL).
+ * Slots >= num_blocks * block_size are skipped rather than written.
+ */
+int pa_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                void* stream);
+
+/*
+ * Bytes of fp32 workspace pa_decode may need for split-context partial
+ * results (running max, sum and unnormalised output per sequence, query head
+ * and context partition).  Depends only on these sizes.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len);
+
+/*
+ * Decode: out[b, h, :] = softmax_j(scale * <q[b, h], K_b[j, h / G]>) . V_b[j, h / G]
+ * over the context_lens[b] tokens of sequence b (which include the token just
+ * stored), where K_b / V_b are gathered through block_tables[b] and
+ * G = num_q_heads / num_kv_heads ("mini-vLLM", project summary: a decode token
+ * attends to its sequence's cached keys and values; "nano-vLLM Part 4",
+ * section 3: decode attention runs over the cached history).
+ *   out, q        [num_seqs, num_q_heads, head_dim]
+ *   context_lens  int32 [num_seqs]
+ *   head_dim      64 or 128
+ *   max_context_len  host upper bound of context_lens (sizes the grid)
+ *   workspace     device memory of at least
+ *                 pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                 max_context_len) bytes, 256-byte aligned; its contents on
+ *                 entry do not matter and are overwritten.
+ * num_seqs == 0 is a no-op.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+              float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * Varlen causal prefill.  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) (Lq of them) and Lk =
+ * cu_seqlens_k[b+1] - cu_seqlens_k[b] keys, all read from the pools through
+ * block_tables[b] (store the new rows with pa_store_kv first).  The new rows
+ * are the last Lq tokens of the sequence, so row i attends to keys
+ * 0 .. (Lk - Lq) + i ("mini-vLLM", project summary: each packed prompt
+ * attends causally to itself; the smzdm Nano-vLLM walk-through, model
+ * implementation details: cu_seqlens_k > cu_seqlens_q marks a prefix-cache
+ * hit).
+ *   out, q        [total_q, num_q_heads, head_dim] packed
+ *   cu_seqlens_q, cu_seqlens_k  int32 [num_seqs + 1]
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of Lq and Lk
+ *   head_dim      64 or 128
+ * bf16 runs on the matrix cores; fp32 runs on the vector ALUs.
+ * num_seqs == 0 or total_q == 0 is a no-op.
+ */
+int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, float scale,
+                      int32_t dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,168 @@
+"""Python binding of libpa's C ABI (include/pa.h): argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, reads their
+shapes and device pointers, and calls the C entry point of the same name on
+the given stream (default: torch's current stream).  Every step of the
+computation runs in libpa's HIP kernels; there is no fallback.  A missing
+library raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PA_OK, PA_E_INVAL, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP = 0, -1, -2, -3, -4
+PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_varlen",
+           "pa_status_string")
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {pa_status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpa (built by paged_kv_cache_85_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m paged_kv_cache_85_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        L.pa_store_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        L.pa_store_kv.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.pa_decode_workspace_bytes.restype = sz
+        L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                f32, i32, vp, sz, vp]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, i32, i32, i32, f32, i32, vp]
+        L.pa_prefill_varlen.restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != PA_OK:
+        raise PAError(fn, rc)
+
+
+def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """k, v: [T, Hkv, D]; pools: [NB, BS, Hkv, D]; slot_mapping: int32 [T]."""
+    torch = _torch()
+    dt = _dtype_code(k_cache)
+    T = k.shape[0]
+    nb, bs, hkv, d = k_cache.shape
+    if tuple(k.shape) != (T, hkv, d) or v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between k/v rows and the pools")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    rc = lib().pa_store_kv(_ptr(k, "k", k_cache.dtype), _ptr(v, "v", k_cache.dtype),
+                           _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache", k_cache.dtype),
+                           _ptr(slot_mapping, "slot_mapping", torch.int32), T, hkv, d, nb, bs,
+                           dt, _stream(stream))
+    _check("pa_store_kv", rc)
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                              max_context_len: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                               max_context_len))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+              scale: float, workspace=None, stream=None) -> None:
+    """q, out: [B, Hq, D]; block_tables: int32 [B, MB]; context_lens: int32 [B].
+    workspace: a device tensor of at least pa_decode_workspace_bytes(...) bytes
+    (allocated here through torch when None)."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    B, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    if workspace is None:
+        n = pa_decode_workspace_bytes(B, hq, d, max_context_len)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().pa_decode(_ptr(out, "out", q.dtype), _ptr(q, "q"),
+                         _ptr(k_cache, "k_cache", q.dtype), _ptr(v_cache, "v_cache", q.dtype),
+                         _ptr(block_tables, "block_tables", torch.int32),
+                         _ptr(context_lens, "context_lens", torch.int32), B, hq, hkv, d, nb, bs,
+                         block_tables.shape[1], int(max_context_len), float(scale), dt,
+                         _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("pa_decode", rc)
+
+
+def pa_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
+                      max_seqlen_q: int, max_seqlen_k: int, scale: float, stream=None) -> None:
+    """q, out: [Tq, Hq, D] packed; cu_seqlens_q/k: int32 [B + 1]; block_tables: int32 [B, MB]."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    tq, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("cu_seqlens must be [B + 1] and block_tables [B, MB]")
+    rc = lib().pa_prefill_varlen(_ptr(out, "out", q.dtype), _ptr(q, "q"),
+                                 _ptr(k_cache, "k_cache", q.dtype),
+                                 _ptr(v_cache, "v_cache", q.dtype),
+                                 _ptr(block_tables, "block_tables", torch.int32),
+                                 _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                                 _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, tq,
+                                 int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, nb, bs,
+                                 block_tables.shape[1], float(scale), dt, _stream(stream))
+    _check("pa_prefill_varlen", rc)

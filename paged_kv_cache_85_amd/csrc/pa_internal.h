@@ -1,0 +1,75 @@
+// Host-side launchers of libpa's kernels (internal; the public ABI is pa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Tokens per split-context partition are a multiple of this; the workspace
+// bound assumes the smallest partition.
+constexpr int kMinPartition = 64;
+
+int launch_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
+                    const int32_t* slot_mapping, int num_tokens, long long row_bytes,
+                    long long num_slots, hipStream_t stream);
+
+// Row-wise attention on the vector ALUs: every query row attends over its own
+// context.  Decode rows come from context_lens; varlen rows (fp32 prefill)
+// derive their context from cu_seqlens.
+struct RowAttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;   // decode mode
+  const int32_t* cu_seqlens_q;   // varlen mode
+  const int32_t* cu_seqlens_k;   // varlen mode
+  void* out;
+  float* ws_o;                   // [rows, Hq, max_parts, D] unnormalised partial outputs
+  float* ws_ml;                  // [rows, Hq, max_parts, 2] (running max in log2 units, sum)
+  int num_rows;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                     // Hq / Hkv
+  int heads_per_wg;              // query heads of one group handled together
+  int head_chunks;               // group / heads_per_wg
+  int max_blocks_per_seq;
+  int num_blocks;
+  int block_size;
+  int block_size_log2;           // -1 when block_size is not a power of two
+  int max_context;               // clamp for per-row context lengths
+  int part_tokens;               // tokens per partition (multiple of 64)
+  int max_parts;
+  float scale_log2;              // scale * log2(e)
+};
+
+int launch_decode(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream);
+int launch_varlen_rows(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  void* out;
+  int num_seqs;
+  int total_q;
+  int max_seqlen_q;
+  int max_seqlen_k;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int block_size;
+  int block_size_log2;
+  float scale_log2;
+};
+
+int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace pa
