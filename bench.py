@@ -1,0 +1,308 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. store 256 new K/V rows + decode (Qwen3-0.6B shapes: 16 q / 8 kv heads,
+     head_dim 128, bf16, block 256, 256 sequences of 100..2048 tokens);
+  2. store + varlen causal prefill (same heads, prompts of 100..1024 tokens
+     packed up to 16384);
+  3. store + prefix-cache prefill (64 sequences sharing a 1024-token cached
+     prefix, 64..512 new tokens each).
+HIP events on the launch stream time every stage of every timed step.  The
+JSON line reports decode HBM GB/s as the headline value (algorithmic bytes:
+K/V of every valid token once, q, out, tables) and the prefill TFLOP/s
+(visible query-key pairs only) beside it, each with its roofline fraction,
+and the fp64 CPU oracle timed on this host's cores for comparison.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(case) -> int:
+    """Algorithmic bytes of one decode call: K and V of every valid token,
+    q and out, block-table entries in use and context lengths."""
+    e = 2 if case.dtype == "bf16" else 4
+    L = case.context_lens.astype(int)
+    kv = 2 * int(L.sum()) * case.num_kv_heads * case.head_dim * e
+    qo = 2 * case.num_seqs * case.num_q_heads * case.head_dim * e
+    idx = 4 * (int(sum(math.ceil(x / case.block_size) for x in L)) + case.num_seqs)
+    return kv + qo + idx
+
+
+def store_bytes(num_rows: int, case) -> int:
+    e = 2 if case.dtype == "bf16" else 4
+    return 2 * 2 * num_rows * case.num_kv_heads * case.head_dim * e + 4 * num_rows
+
+
+def prefill_flops(case) -> int:
+    """4 * D * Hq per visible (query, key) pair: QK^T and PV, 2 FLOP per MAC."""
+    ql, kl = case.q_lens.astype(int), case.k_lens.astype(int)
+    pairs = sum(int(q) * (int(k) - int(q)) + int(q) * (int(q) + 1) // 2 for q, k in zip(ql, kl))
+    return 4 * case.head_dim * case.num_q_heads * pairs
+
+
+def prefill_bytes(case) -> int:
+    """Q and O once, K and V of every distinct key once (a shared prefix once)."""
+    e = 2
+    qo = 2 * case.total_q * case.num_q_heads * case.head_dim * e
+    if case.shared_prefix:
+        keys = int(case.prefix_k.shape[0]) + case.total_q
+    else:
+        keys = int(case.k_lens.sum())
+    return qo + 2 * keys * case.num_kv_heads * case.head_dim * e
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_85_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources") != kernel_sources_digest():
+        return None
+    try:
+        return int(float(kv["bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_oracle_baseline(dec, pre4):
+    """The fp64 oracle, untuned, on this host: decode over the whole decode
+    workload and prefill over the varlen workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    with threadpool_limits(limits=threads):
+        used = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+        kc, vc = oracle.store_kv(dec.k_cache, dec.v_cache, dec.k_new, dec.v_new,
+                                 dec.slot_mapping)
+        t = time.perf_counter()
+        oracle.decode(dec.q, kc, vc, dec.block_tables, dec.context_lens, dec.scale, dec.dtype)
+        t_dec = time.perf_counter() - t
+        del kc, vc
+        kc, vc = oracle.store_kv(pre4.k_cache, pre4.v_cache, pre4.k_new, pre4.v_new,
+                                 pre4.slot_mapping)
+        t = time.perf_counter()
+        oracle.prefill_varlen(pre4.q, kc, vc, pre4.block_tables, pre4.cu_seqlens_q,
+                              pre4.cu_seqlens_k, pre4.scale, pre4.dtype)
+        t_pre = time.perf_counter() - t
+    return {
+        "decode": {"value": decode_bytes(dec) / t_dec / 1e9, "unit": "GB/s", "cores": used,
+                   "kind": "oracle", "seconds": t_dec,
+                   "sample": f"whole decode workload: {dec.num_seqs} sequences, "
+                             f"{int(dec.context_lens.sum())} cached tokens (fp64 numpy)"},
+        "prefill": {"value": prefill_flops(pre4) / t_pre / 1e12, "unit": "TFLOP/s",
+                    "cores": used, "kind": "oracle", "seconds": t_pre,
+                    "sample": f"whole varlen prefill workload: {pre4.num_seqs} prompts, "
+                              f"{pre4.total_q} tokens (fp64 numpy)"},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(each GPU would run its own share of heads or sequences)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_85_amd as pa
+    from synth import make_case
+
+    if not os.path.exists(pa.LIB_PATH):
+        from paged_kv_cache_85_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        return t.to(dev)
+
+    log("generating inputs")
+    dec = make_case(3)
+    pre4 = make_case(4)
+    pre5 = make_case(5)
+
+    class Staged:
+        pass
+
+    def stage(case, kind):
+        s = Staged()
+        s.case = case
+        s.kc, s.vc = up(case.k_cache), up(case.v_cache)
+        s.k_new, s.v_new, s.slots = up(case.k_new), up(case.v_new), up(case.slot_mapping)
+        s.q = up(case.q)
+        s.out = torch.empty_like(s.q)
+        s.bt = up(case.block_tables)
+        if kind == "decode":
+            s.cl = up(case.context_lens)
+            n = pa.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
+                                             case.max_context_len)
+            s.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        else:
+            s.cq, s.ck = up(case.cu_seqlens_q), up(case.cu_seqlens_k)
+        return s
+
+    log("uploading")
+    D = stage(dec, "decode")
+    P4 = stage(pre4, "prefill")
+    P5 = stage(pre5, "prefill")
+    stream = torch.cuda.current_stream()
+
+    def store(s):
+        pa.pa_store_kv(s.k_new, s.v_new, s.kc, s.vc, s.slots, stream=stream)
+
+    def decode(s):
+        c = s.case
+        pa.pa_decode(s.out, s.q, s.kc, s.vc, s.bt, s.cl, c.max_context_len, float(c.scale),
+                     workspace=s.ws, stream=stream)
+
+    def prefill(s):
+        c = s.case
+        pa.pa_prefill_varlen(s.out, s.q, s.kc, s.vc, s.bt, s.cq, s.ck, c.max_seqlen_q,
+                             c.max_seqlen_k, float(c.scale), stream=stream)
+
+    stages = [("store_decode", lambda: store(D)), ("decode", lambda: decode(D)),
+              ("store_prefill", lambda: store(P4)), ("prefill", lambda: prefill(P4)),
+              ("store_prefix", lambda: store(P5)), ("prefix_prefill", lambda: prefill(P5))]
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(stages):
+            if events is not None:
+                events[i].record(stream)
+            fn()
+        if events is not None:
+            events[-1].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+                  for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(all_events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    dur = {name: [] for name, _ in stages}
+    for ev in all_events:
+        for i, (name, _) in enumerate(stages):
+            dur[name].append(ev[i].elapsed_time(ev[i + 1]) * 1e-3)   # seconds
+    avg = {k: float(np.mean(v)) for k, v in dur.items()}
+    med = {k: float(np.median(v)) for k, v in dur.items()}
+
+    dec_bytes = decode_bytes(dec)
+    dec_gbs = dec_bytes / avg["decode"] / 1e9
+    f4, f5 = prefill_flops(pre4), prefill_flops(pre5)
+    t4, t5 = f4 / avg["prefill"] / 1e12, f5 / avg["prefix_prefill"] / 1e12
+    dec_path_bytes = dec_bytes + store_bytes(dec.num_seqs, dec)
+    dec_path_s = avg["decode"] + avg["store_decode"]
+
+    traffic = measured_traffic("decode_qwen3_0.6b")
+    result = {
+        "metric": "paged-attn decode HBM GB/s & prefill TFLOP/s (% of peak), Qwen3-0.6B shapes",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, shuffled physical block IDs)",
+        "config": {
+            "workload": "Qwen3-0.6B attention shapes: decode 256 seqs L~U[100,2048] + "
+                        "varlen prefill <=16384 tokens + 64-seq 1024-token prefix-cache prefill",
+            "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 128, "block_size": 256,
+            "decode_seqs": dec.num_seqs, "decode_cached_tokens": int(dec.context_lens.sum()),
+            "prefill_prompts": pre4.num_seqs, "prefill_tokens": pre4.total_q,
+            "prefix_seqs": pre5.num_seqs, "prefix_new_tokens": pre5.total_q,
+            "parallelism": "none (one GPU)",
+        },
+        "roofline": {
+            "kernel": "pa_decode (partition + combine kernels)",
+            "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_us": round(avg["decode"] * 1e6, 2),
+            "median_launch_us": round(med["decode"] * 1e6, 2),
+        },
+        "roofline_prefill": {
+            "varlen": {"bound": "mfma", "achieved": round(t4, 2), "peak": BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(t4 / BF16_PEAK_TFLOPS, 4),
+                       "flops_per_launch": f4, "avg_launch_us": round(avg["prefill"] * 1e6, 2),
+                       "hbm_frac": round(prefill_bytes(pre4) / avg["prefill"] / 1e9
+                                         / HBM_PEAK_GBS, 4)},
+            "prefix_cache": {"bound": "mfma", "achieved": round(t5, 2),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(t5 / BF16_PEAK_TFLOPS, 4), "flops_per_launch": f5,
+                             "avg_launch_us": round(avg["prefix_prefill"] * 1e6, 2)},
+        },
+        "stages_us": {k: round(v * 1e6, 2) for k, v in avg.items()},
+        "decode_path_gbs": round(dec_path_bytes / dec_path_s / 1e9, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle")
+        cpu = cpu_oracle_baseline(dec, pre4)
+        result["cpu_baseline"] = cpu["decode"]
+        result["cpu_baseline_prefill"] = cpu["prefill"]
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -275,7 +275,7 @@ class PrefillCase:
 # --------------------------------------------------------------------------- paging
 
 def _allocate(rng: np.random.Generator, shared_blocks: int, private_blocks: Sequence[int],
-              num_blocks: Optional[int], free_frac: float):
+              num_blocks: Optional[int], free_frac: float, width: int = 0):
     """Hand out physical block IDs as a shuffled free list would: a seeded
     permutation of the pool, taken in sequence order.  Returns the block
     tables (unused entries point at a spare block, so a reader that strays
@@ -288,7 +288,7 @@ def _allocate(rng: np.random.Generator, shared_blocks: int, private_blocks: Sequ
     ids = rng.permutation(num_blocks).astype(np.int32)
     shared = ids[:shared_blocks]
     spare = int(ids[need]) if num_blocks > need else int(ids[0])
-    nb_max = max([shared_blocks + p for p in private_blocks] + [1])
+    nb_max = max([shared_blocks + p for p in private_blocks] + [1, width])
     tables = np.full((len(private_blocks), nb_max), spare, np.int32)
     pos = shared_blocks
     for b, p in enumerate(private_blocks):
@@ -316,14 +316,16 @@ def _place(pool: np.ndarray, slots: np.ndarray, rows: np.ndarray) -> None:
 # --------------------------------------------------------------------------- decode
 
 def _page_decode(spec: DecodeSpec, lens: np.ndarray, hist_k, hist_v, k_new, v_new, q,
-                 bs: int, perm_seed: int, poison: str, fixed_nb: Optional[int]) -> DecodeCase:
+                 bs: int, perm_seed: int, poison: str, fixed_nb: Optional[int],
+                 width: int = 0) -> DecodeCase:
     hkv, d, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     B = int(lens.size)
     hist_n = lens - 1
     hist_off = np.zeros(B + 1, np.int64)
     np.cumsum(hist_n, out=hist_off[1:])
     per_seq = [int(math.ceil(int(L) / bs)) for L in lens]
-    tables, nb = _allocate(_rng(perm_seed, _S_PAGING), 0, per_seq, fixed_nb, spec.free_frac)
+    tables, nb = _allocate(_rng(perm_seed, _S_PAGING), 0, per_seq, fixed_nb, spec.free_frac,
+                           width)
     seq = np.repeat(np.arange(B), hist_n)
     pos = np.arange(int(hist_off[-1])) - np.repeat(hist_off[:-1], hist_n)
     hslots = _slots(tables, seq, pos, bs)
@@ -376,9 +378,11 @@ def make_decode(spec: DecodeSpec, seed: int, block_size: Optional[int] = None,
 
 
 def decode_subset(case: DecodeCase, seqs: Sequence[int], perm_seed: int = 0,
-                  block_size: Optional[int] = None) -> DecodeCase:
+                  block_size: Optional[int] = None, table_width: int = 0) -> DecodeCase:
     """The same sequences (same content, fresh paging), alone or in another
-    batch order: the "batched versus alone" comparison of the mini-vLLM page."""
+    batch order: the "batched versus alone" comparison of the mini-vLLM page.
+    ``table_width`` pads the block tables (with a spare block) to at least
+    that many columns."""
     seqs = list(seqs)
     lens = case.context_lens[seqs].astype(np.int64)
     hk = [case.hist_k[case.hist_off[b]:case.hist_off[b + 1]] for b in seqs]
@@ -388,14 +392,14 @@ def decode_subset(case: DecodeCase, seqs: Sequence[int], perm_seed: int = 0,
     bs = case.block_size if block_size is None else block_size
     return _page_decode(case.spec, lens, hk, hv, case.k_new[seqs].copy(),
                         case.v_new[seqs].copy(), case.q[seqs].copy(), bs, perm_seed,
-                        case.poison, None)
+                        case.poison, None, table_width)
 
 
 # --------------------------------------------------------------------------- prefill
 
 def _page_prefill(spec: PrefillSpec, ql: np.ndarray, pl: np.ndarray, shared: bool,
                   prefix_k, prefix_v, prefix_off, k_new, v_new, q, bs: int, perm_seed: int,
-                  poison: str) -> PrefillCase:
+                  poison: str, width: int = 0) -> PrefillCase:
     hkv, d, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     B = int(ql.size)
     P = int(prefix_k.shape[0]) if shared else 0
@@ -408,7 +412,7 @@ def _page_prefill(spec: PrefillSpec, ql: np.ndarray, pl: np.ndarray, shared: boo
     else:
         sb = 0
         private = [int(math.ceil(int(kl[b]) / bs)) for b in range(B)]
-    tables, nb = _allocate(_rng(perm_seed, _S_PAGING), sb, private, None, spec.free_frac)
+    tables, nb = _allocate(_rng(perm_seed, _S_PAGING), sb, private, None, spec.free_frac, width)
     k_cache = _empty_pool(nb, bs, hkv, d, dt, poison, "k")
     v_cache = _empty_pool(nb, bs, hkv, d, dt, poison, "v")
     if shared:
@@ -501,7 +505,7 @@ def make_prefill(spec: PrefillSpec, seed: int, block_size: Optional[int] = None,
 
 
 def prefill_subset(case: PrefillCase, seqs: Sequence[int], perm_seed: int = 0,
-                   block_size: Optional[int] = None) -> PrefillCase:
+                   block_size: Optional[int] = None, table_width: int = 0) -> PrefillCase:
     """The same sequences (same content, fresh paging) alone or reordered."""
     seqs = list(seqs)
     ql = case.q_lens[seqs].astype(np.int64)
@@ -524,7 +528,8 @@ def prefill_subset(case: PrefillCase, seqs: Sequence[int], perm_seed: int = 0,
         np.cumsum(pl, out=poff[1:])
     bs = case.block_size if block_size is None else block_size
     return _page_prefill(case.spec, ql, pl, case.shared_prefix, pk, pv, poff, rows(case.k_new),
-                         rows(case.v_new), rows(case.q), bs, perm_seed, case.poison)
+                         rows(case.v_new), rows(case.q), bs, perm_seed, case.poison,
+                         table_width)
 
 
 def make_case(config: int, seed: Optional[int] = None, **kw):

@@ -6,6 +6,9 @@ same host arrays.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 TOL = {"f32": (1e-5, None), "bf16": (2e-2, 2e-3)}   # (max-abs, mean-abs) vs the fp64 oracle
@@ -104,6 +107,11 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -
     mean_abs = float(err.mean()) if err.size else 0.0
     tmax, tmean = TOL[dtype]
     say(f"{what}: max_abs={max_abs:.3e} mean_abs={mean_abs:.3e}")
+    log = os.environ.get("PA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": what, "dtype": dtype, "max_abs": max_abs,
+                                "mean_abs": mean_abs, "n": int(err.size)}) + "\n")
     assert max_abs <= tmax, f"{what}: max-abs {max_abs} > {tmax}"
     if tmean is not None:
         assert mean_abs <= tmean, f"{what}: mean-abs {mean_abs} > {tmean}"

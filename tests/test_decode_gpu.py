@@ -76,7 +76,8 @@ def test_decode_permutation_and_batching_bitwise():
     permuted, _, _ = run_decode(make_case(2, perm_seed=99))
     assert np.array_equal(bits(permuted), ref)
     for b in (0, 5, 31):
-        alone, _, _ = run_decode(decode_subset(case, [b], perm_seed=b + 1),
+        alone, _, _ = run_decode(decode_subset(case, [b], perm_seed=b + 1,
+                                               table_width=case.max_blocks_per_seq),
                                  max_context_len=case.max_context_len)
         assert np.array_equal(bits(alone)[0], ref[b]), b
     rev = list(range(case.num_seqs))[::-1]
@@ -91,7 +92,8 @@ def test_decode_sampled_full_size_alone():
     ref, _, _ = run_decode(case)
     ref = bits(ref)
     for b in (0, 100, 255):
-        alone, _, _ = run_decode(decode_subset(case, [b], perm_seed=3),
+        alone, _, _ = run_decode(decode_subset(case, [b], perm_seed=3,
+                                               table_width=case.max_blocks_per_seq),
                                  max_context_len=case.max_context_len)
         assert np.array_equal(bits(alone)[0], ref[b])
 
