@@ -62,26 +62,33 @@ struct ElemBF16 {
   }
 };
 
-template <typename E, int D, int HG, bool VARLEN>
-__global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
+// BIG: power-of-two blocks of >= 64 tokens, so a pipeline stage never
+// straddles a block and one scalar table read serves a stage.  Otherwise
+// decode stages its partition's block IDs in LDS (one read at the start, so
+// lookups never wait behind the K/V stream) and varlen rows read the table
+// per lane.
+template <typename E, int D, int HG, bool VARLEN, bool BIG>
+__global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   typedef typename E::storage T;
   constexpr int EPL = E::EPL;
-  constexpr int LPR = D / EPL;  // lanes per K/V head row
+  constexpr int LPR = D / EPL;   // lanes per K/V head row
   constexpr int RPS = 64 / LPR;  // token rows per load instruction
-  constexpr int S = 64 / RPS;    // load steps per 64-token chunk
+  constexpr int SS = 8;          // load steps per pipeline stage
+  constexpr int SUB = SS * RPS;  // tokens per pipeline stage (16..64)
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int c = lane % LPR;
   const int r = lane / LPR;
 
-  // blockIdx.x = (row * Y + y) * max_parts + p, Y = kv heads * head chunks
+  // blockIdx.x = (row * max_parts + p) * Y + y, Y = kv heads * head chunks:
+  // the heads of one partition are adjacent, so they are dispatched together
+  // and read neighbouring bytes of the same token rows.
   const int Y = a.num_kv_heads * a.head_chunks;
   int x = blockIdx.x;
-  const int p = x % a.max_parts;
-  x /= a.max_parts;
   const int y = x % Y;
-  const int row = x / Y;
+  x /= Y;
+  const int p = x % a.max_parts;
+  const int row = x / a.max_parts;
   const int g = y / a.head_chunks;
   const int h0 = g * a.group + (y % a.head_chunks) * HG;
 
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
   T* out = reinterpret_cast<T*>(a.out);
   if (L <= 0) {  // violated precondition: define the output as zeros
     if (p == 0)
-      for (int idx = threadIdx.x; idx < HG * D; idx += 256)
+      for (int idx = lane; idx < HG * D; idx += 64)
         E::store(out + ((long)row * a.num_q_heads + h0) * D + idx, 0.f);
     return;
   }
@@ -117,13 +124,25 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nb = a.num_blocks;
-  const bool big_blocks = bs_log2 >= 6;  // a 64-token chunk never straddles a block
+
+  constexpr bool kLdsTable = !BIG && !VARLEN;
+  constexpr int kMaxTable = kLdsTable ? 256 : 1;  // blocks of one 256-token partition
+  __shared__ int s_bt[kMaxTable];
+  int first_blk = 0;
+  if constexpr (kLdsTable) {
+    first_blk = bs_log2 >= 0 ? (tok_begin >> bs_log2) : tok_begin / bs;
+    const int last_blk = bs_log2 >= 0 ? ((tok_end - 1) >> bs_log2) : (tok_end - 1) / bs;
+    for (int i = lane; i <= last_blk - first_blk && i < kMaxTable; i += 64)
+      s_bt[i] = clamp_block(bt[first_blk + i], nb);
+    __syncthreads();
+  }
 
   // Queries of the HG heads, pre-multiplied by scale * log2(e): scores come
   // out in log2 units and the softmax uses exp2.
   float qf[HG][EPL];
   {
-    const T* qp = reinterpret_cast<const T*>(a.q) + ((long)row * a.num_q_heads + h0) * D + c * EPL;
+    const T* qp =
+        reinterpret_cast<const T*>(a.q) + ((long)row * a.num_q_heads + h0) * D + c * EPL;
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
       E::widen(*reinterpret_cast<const uint4*>(qp + h * D), qf[h]);
@@ -143,40 +162,62 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
 
   const T* kc = reinterpret_cast<const T*>(a.k_cache);
   const T* vc = reinterpret_cast<const T*>(a.v_cache);
-  const long slot_elems = (long)a.num_kv_heads * D;
-  const long head_off = (long)g * D + c * EPL;
+  const int slot_elems = a.num_kv_heads * D;  // elements per token slot
+  const int head_off = g * D + c * EPL;
+  unsigned big_off[BIG ? SS : 1];
+  if constexpr (BIG) {
+#pragma unroll
+    for (int s = 0; s < SS; ++s)
+      big_off[s] = (unsigned)((s * RPS + r) * slot_elems + c * EPL) * (unsigned)sizeof(T);
+  }
 
-  for (int t0 = tok_begin + w * 64; t0 < tok_end; t0 += 256) {
-    long sbase = 0;
-    if (big_blocks) {
+  // Load one stage of SUB tokens.  Lanes past the partition's end read the
+  // last valid token instead (always a written row, never poison) and their
+  // scores are masked, so every load is unconditional and in bounds.
+  auto load = [&](uint4 (&kr)[SS], uint4 (&vr)[SS], int t0) {
+    const int nvalid = tok_end - t0;  // >= 1
+    if constexpr (BIG) {
+      // Wave-uniform base of this stage's rows for head g plus loop-invariant
+      // per-lane byte offsets.  A stage lies inside one block, so rows past
+      // the partition's end are still pool slots of that block (possibly
+      // poison); compute() masks their scores and zeroes their values.
       const int blk = clamp_block(bt[t0 >> bs_log2], nb);
-      sbase = ((long)blk << bs_log2) - (long)((t0 >> bs_log2) << bs_log2);
-    }
-    uint4 kr[S], vr[S];
+      const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
+      const char* kp = reinterpret_cast<const char*>(kc + base);
+      const char* vp = reinterpret_cast<const char*>(vc + base);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int j = t0 + s * RPS + r;
-      if (j < tok_end) {
-        long slot;
-        if (big_blocks) {
-          slot = sbase + j;
-        } else if (bs_log2 >= 0) {
-          slot = ((long)clamp_block(bt[j >> bs_log2], nb) << bs_log2) + (j & (bs - 1));
+      for (int s = 0; s < SS; ++s) kr[s] = *reinterpret_cast<const uint4*>(kp + big_off[s]);
+#pragma unroll
+      for (int s = 0; s < SS; ++s) vr[s] = *reinterpret_cast<const uint4*>(vp + big_off[s]);
+    } else {
+      long off[SS];
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const int j = t0 + min(s * RPS + r, nvalid - 1);
+        int blk, in_blk;
+        if (bs_log2 >= 0) {
+          blk = j >> bs_log2;
+          in_blk = j & (bs - 1);
         } else {
-          slot = (long)clamp_block(bt[j / bs], nb) * bs + j % bs;
+          blk = j / bs;
+          in_blk = j - blk * bs;
         }
-        const long off = slot * slot_elems + head_off;
-        kr[s] = *reinterpret_cast<const uint4*>(kc + off);
-        vr[s] = *reinterpret_cast<const uint4*>(vc + off);
-      } else {
-        kr[s] = make_uint4(0, 0, 0, 0);
-        vr[s] = make_uint4(0, 0, 0, 0);
+        if constexpr (kLdsTable) blk = s_bt[blk - first_blk];
+        else blk = clamp_block(bt[blk], nb);
+        off[s] = ((long)blk * bs + in_blk) * slot_elems + head_off;
       }
-    }
-
-    float sc[HG][S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+      for (int s = 0; s < SS; ++s) kr[s] = *reinterpret_cast<const uint4*>(kc + off[s]);
+#pragma unroll
+      for (int s = 0; s < SS; ++s) vr[s] = *reinterpret_cast<const uint4*>(vc + off[s]);
+    }
+  };
+
+  // Fold one stage into the running (max, sum, output) of this lane's row.
+  auto compute = [&](const uint4 (&kr)[SS], const uint4 (&vr)[SS], int t0) {
+    float sc[HG][SS];
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
       float kf[EPL];
       E::widen(kr[s], kf);
 #pragma unroll
@@ -188,20 +229,26 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
       }
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const bool valid = t0 + s * RPS + r < tok_end;
+    for (int s = 0; s < SS; ++s)
 #pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float v = group_sum<LPR>(sc[h][s]);
-        sc[h][s] = valid ? v : -INFINITY;
+      for (int h = 0; h < HG; ++h) sc[h][s] = group_sum<LPR>(sc[h][s]);
+    uint4 vz[SS];
+#pragma unroll
+    for (int s = 0; s < SS; ++s) vz[s] = vr[s];
+    if (t0 + SUB > tok_end) {  // last, partial stage: rows past the end do not count
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const bool valid = t0 + s * RPS + r < tok_end;
+#pragma unroll
+        for (int h = 0; h < HG; ++h) sc[h][s] = valid ? sc[h][s] : -INFINITY;
+        if (!valid) vz[s] = make_uint4(0, 0, 0, 0);
       }
     }
-
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
       float mx = sc[h][0];
 #pragma unroll
-      for (int s = 1; s < S; ++s) mx = fmaxf(mx, sc[h][s]);
+      for (int s = 1; s < SS; ++s) mx = fmaxf(mx, sc[h][s]);
       const float mn = fmaxf(m[h], mx);
       const float alpha = fast_exp2(m[h] - mn);
       m[h] = mn;
@@ -209,7 +256,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
+      for (int s = 0; s < SS; ++s) {
         const float pr = fast_exp2(sc[h][s] - mn);
         lsum += pr;
         sc[h][s] = pr;
@@ -217,17 +264,40 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
       l[h] = lsum;
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < SS; ++s) {
       float vf[EPL];
-      E::widen(vr[s], vf);
+      E::widen(vz[s], vf);
 #pragma unroll
       for (int h = 0; h < HG; ++h)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(sc[h][s], vf[e], o[h][e]);
     }
+  };
+
+  // Two register stages: the next stage's loads are in flight while the
+  // current one is folded in.  The prefetch is unconditional (at the end it
+  // re-reads the last stage, which is cached) so that the compiler can count
+  // outstanding loads exactly and never waits for the stage in flight.
+  uint4 kA[SS], vA[SS], kB[SS], vB[SS];
+  const int last_t0 = tok_begin + ((tok_end - tok_begin - 1) / SUB) * SUB;
+  int t0 = tok_begin;
+  load(kA, vA, t0);
+  // sched_barrier keeps the scheduler from sinking the prefetch below the
+  // fold of the current stage.
+  for (;;) {
+    load(kB, vB, min(t0 + SUB, last_t0));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kA, vA, t0);
+    if (t0 >= last_t0) break;
+    t0 += SUB;
+    load(kA, vA, min(t0 + SUB, last_t0));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kB, vB, t0);
+    if (t0 >= last_t0) break;
+    t0 += SUB;
   }
 
-  // Merge the RPS independent row states of the wave (lanes c, c + LPR, ...).
+  // Merge the RPS independent row states (lanes c, c + LPR, ...).
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
     float M = m[h];
@@ -248,44 +318,23 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnArgs a) {
     l[h] = lw;
   }
 
-  // Merge the four waves through LDS and finish (or emit a partial).
-  __shared__ float s_o[4][HG][D];
-  __shared__ float s_ml[4][HG][2];
-  if (r == 0) {
+  if (r != 0) return;
 #pragma unroll
-    for (int h = 0; h < HG; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[w][h][c * EPL + e] = o[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      s_ml[w][h][0] = m[h];
-      s_ml[w][h][1] = l[h];
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < HG * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float M = s_ml[0][h][0];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, s_ml[ww][h][0]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float wg = fast_exp2(s_ml[ww][h][0] - M);
-      acc = fmaf(s_o[ww][h][d], wg, acc);
-      lsum = fmaf(s_ml[ww][h][1], wg, lsum);
-    }
+  for (int h = 0; h < HG; ++h) {
     const long oh = (long)row * a.num_q_heads + h0 + h;
     if (nparts == 1) {
-      E::store(out + oh * D + d, acc / lsum);
+      const float inv = 1.f / l[h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) E::store(out + oh * D + c * EPL + e, o[h][e] * inv);
     } else {
-      a.ws_o[(oh * a.max_parts + p) * D + d] = acc;
-      if (d == 0) {
-        a.ws_ml[(oh * a.max_parts + p) * 2] = M;
-        a.ws_ml[(oh * a.max_parts + p) * 2 + 1] = lsum;
+      float* po = a.ws_o + (oh * a.max_parts + p) * D + c * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(po + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2],
+                                                         o[h][e + 3]);
+      if (c == 0) {
+        a.ws_ml[(oh * a.max_parts + p) * 2] = m[h];
+        a.ws_ml[(oh * a.max_parts + p) * 2 + 1] = l[h];
       }
     }
   }
@@ -314,18 +363,18 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(RowAttnArgs a) {
   E::store(reinterpret_cast<T*>(a.out) + oh * D + threadIdx.x, acc / lsum);
 }
 
-template <typename E, int D, bool VARLEN>
+template <typename E, int D, bool VARLEN, bool BIG>
 static int launch_rows_hg(const RowAttnArgs& a, hipStream_t stream) {
   const long long grid =
       (long long)a.num_rows * a.num_kv_heads * a.head_chunks * a.max_parts;
   if (grid <= 0) return 0;
   if (grid > 0x7fffffffLL) return -1;
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(64);
   switch (a.heads_per_wg) {
 #define PA_HG_CASE(N)                                                                        \
   case N:                                                                                    \
     if constexpr (N <= (D == 64 ? 8 : 4))                                                    \
-      hipLaunchKernelGGL((row_attn_kernel<E, D, N, VARLEN>), g, blk, 0, stream, a);          \
+      hipLaunchKernelGGL((row_attn_kernel<E, D, N, VARLEN, BIG>), g, blk, 0, stream, a);     \
     else                                                                                     \
       return -1;                                                                             \
     break;
@@ -344,18 +393,24 @@ static int launch_rows_hg(const RowAttnArgs& a, hipStream_t stream) {
   return 0;
 }
 
+template <typename E, int D, bool VARLEN>
+static int launch_rows_mode(const RowAttnArgs& a, hipStream_t stream) {
+  if (a.block_size_log2 >= 6) return launch_rows_hg<E, D, VARLEN, true>(a, stream);
+  return launch_rows_hg<E, D, VARLEN, false>(a, stream);
+}
+
 static int dispatch_rows(const RowAttnArgs& a, int head_dim, int dtype, bool varlen,
                          hipStream_t stream) {
   if (dtype == 0) {
     if (head_dim == 64)
-      return varlen ? launch_rows_hg<ElemF32, 64, true>(a, stream)
-                    : launch_rows_hg<ElemF32, 64, false>(a, stream);
-    return varlen ? launch_rows_hg<ElemF32, 128, true>(a, stream)
-                  : launch_rows_hg<ElemF32, 128, false>(a, stream);
+      return varlen ? launch_rows_mode<ElemF32, 64, true>(a, stream)
+                    : launch_rows_mode<ElemF32, 64, false>(a, stream);
+    return varlen ? launch_rows_mode<ElemF32, 128, true>(a, stream)
+                  : launch_rows_mode<ElemF32, 128, false>(a, stream);
   }
   if (varlen) return -1;  // bf16 prefill runs on the matrix cores
-  return head_dim == 64 ? launch_rows_hg<ElemBF16, 64, false>(a, stream)
-                        : launch_rows_hg<ElemBF16, 128, false>(a, stream);
+  return head_dim == 64 ? launch_rows_mode<ElemBF16, 64, false>(a, stream)
+                        : launch_rows_mode<ElemBF16, 128, false>(a, stream);
 }
 
 int launch_decode(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream) {
