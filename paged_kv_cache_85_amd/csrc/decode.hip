@@ -1,32 +1,40 @@
 // Decode attention over a paged KV cache on the vector ALUs, split over the
-// context ("flash-decoding" style partitions) with an online softmax.
+// context with an online softmax.
 //
 // A decode query is one token per sequence attending to that sequence's
 // cached keys and values ("mini-vLLM", project summary), read through the
 // sequence's block table ("nano-vLLM Part 4", section 3: decode attention
 // over the cached history).  The work is HBM-bound (about 2 FLOP per byte of
-// bf16 KV at a query group of 2), so the kernel is organised around the
-// memory stream rather than the matrix cores:
+// bf16 KV at a query group of 2), so the kernels are organised around the
+// memory stream, not the matrix cores:
 //
-//  * one workgroup = 4 waves = one (sequence, KV head, context partition);
-//    the query heads of the KV head's group (up to HG of them) share every
-//    K/V row loaded, so each KV byte is read once per group;
-//  * a wave covers 64 tokens per iteration; each lane loads 16 contiguous
-//    bytes of a token's head row, LPR lanes cover the row and RPS rows load
-//    per instruction, so every load is a fully used 16-byte access and a wave
-//    keeps 2 x 64 x 16 B x (64 / RPS) bytes in flight;
+//  * the unit of work is an item = (sequence, 256-token context partition,
+//    KV head); the query heads of the KV head's group (up to HG of them)
+//    share every K/V row loaded, so each KV byte is read once per group;
+//  * one wave folds an item in stages of SUB tokens; each lane loads 16
+//    contiguous bytes of a token's head row, LPR lanes cover the row and RPS
+//    rows load per instruction (fully used 16-byte accesses);
 //  * q.k partial dot products are reduced across the LPR lanes of a row with
 //    DPP (quad permutes and row mirrors), which leaves every lane of the row
 //    holding the full score, so probabilities need no broadcast;
 //  * each lane row keeps its own running max / sum / output (an independent
-//    online softmax), merged across rows and waves once at the end;
-//  * partitions of several 64-token chunks write unnormalised partials
-//    (output, max, sum) to the workspace; a small combine kernel rescales and
-//    sums them.  A sequence that fits one partition is finished in place.
+//    online softmax), merged across rows once per item;
+//  * an item of a sequence with several partitions writes an unnormalised
+//    partial (output, max, sum) to the workspace; a small combine kernel
+//    rescales and sums them.  A one-partition sequence is finished in place.
+//    The partition size is fixed, so a row's arithmetic depends only on its
+//    own tokens: results are bitwise independent of the batch, the physical
+//    block IDs and the block size.
 //
-// The same kernel, in "varlen" mode, computes fp32 prefill rows: row i of a
-// sequence with Lq new and Lk total tokens is a decode over its first
-// Lk - Lq + i + 1 keys.
+// Large power-of-two blocks (>= 64 tokens; 256 in the Qwen3 workloads) run a
+// persistent kernel: one wave per resident slot walks an equal, contiguous
+// share of all items, and a ring of register stages keeps NBUF - 1 stages in
+// flight across item boundaries, so the memory stream never drains between
+// items and no launch slot is spent on empty partitions.  Each stage is read
+// through a raw buffer descriptor that covers exactly its valid rows (rows
+// past the end read zero).  Other block sizes, and the fp32 prefill rows
+// ("varlen": row i of a sequence with Lq new and Lk total tokens is a decode
+// over its first Lk - Lq + i + 1 keys), use one wave per item.
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -62,27 +70,187 @@ struct ElemBF16 {
   }
 };
 
-// BIG: power-of-two blocks of >= 64 tokens, so a pipeline stage never
-// straddles a block and one scalar table read serves a stage.  Otherwise
-// decode stages its partition's block IDs in LDS (one read at the start, so
-// lookups never wait behind the K/V stream) and varlen rows read the table
-// per lane.
+#ifndef PA_DECODE_STAGE_STEPS
+#define PA_DECODE_STAGE_STEPS 4
+#endif
+#ifndef PA_DECODE_STAGES
+#define PA_DECODE_STAGES 3
+#endif
+constexpr int kStageSteps = PA_DECODE_STAGE_STEPS;  // load steps per stage
+constexpr int kStages = PA_DECODE_STAGES;           // register stages in the ring
+
+// Raw buffer descriptor (GFX9 family: dword3 = 0x00020000) over `bytes`
+// bytes at `base`; loads at offsets past the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Online-softmax state of one wave for HG query heads (lane = row r of RPS,
+// column c of LPR).
+template <typename E, int D, int HG>
+struct RowFold {
+  static constexpr int EPL = E::EPL;
+  static constexpr int LPR = D / EPL;  // lanes per K/V head row
+  static constexpr int RPS = 64 / LPR;  // token rows per load instruction
+  static constexpr int SS = kStageSteps;
+  static constexpr int SUB = SS * RPS;  // tokens per stage
+  typedef typename E::storage T;
+
+  float qf[HG][EPL];  // queries pre-multiplied by scale * log2(e)
+  float m[HG], l[HG], o[HG][EPL];
+
+  __device__ __forceinline__ void set_q(const uint4 (&raw)[HG], float scale_log2) {
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      E::widen(raw[h], qf[h]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] *= scale_log2;
+    }
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      m[h] = kNegBig;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    }
+  }
+
+  // Fold one stage (tokens t0 .. t0 + SUB - 1, of which those < tok_end
+  // count).  Rows past the end hold zeros or a copy of a valid row: finite
+  // values whose scores are masked here, so they add nothing.
+  __device__ __forceinline__ void fold(const uint4 (&kr)[SS], const uint4 (&vr)[SS], int t0,
+                                       int tok_end, int r) {
+    float sc[HG][SS];
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      float kf[EPL];
+      E::widen(kr[s], kf);
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[h][e], kf[e], acc);
+        sc[h][s] = acc;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SS; ++s)
+#pragma unroll
+      for (int h = 0; h < HG; ++h) sc[h][s] = group_sum<LPR>(sc[h][s]);
+    if (t0 + SUB > tok_end) {
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const bool valid = t0 + s * RPS + r < tok_end;
+#pragma unroll
+        for (int h = 0; h < HG; ++h) sc[h][s] = valid ? sc[h][s] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      float mx = sc[h][0];
+#pragma unroll
+      for (int s = 1; s < SS; ++s) mx = fmaxf(mx, sc[h][s]);
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      float lsum = l[h] * alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const float pr = fast_exp2(sc[h][s] - mn);
+        lsum += pr;
+        sc[h][s] = pr;
+      }
+      l[h] = lsum;
+    }
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      float vf[EPL];
+      E::widen(vr[s], vf);
+#pragma unroll
+      for (int h = 0; h < HG; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(sc[h][s], vf[e], o[h][e]);
+    }
+  }
+
+  // Merge the RPS independent row states (lanes c, c + LPR, ...) and write
+  // the item: normalised output when the sequence has one partition, else an
+  // unnormalised partial.  Lanes of row 0 hold the merged state.
+  __device__ __forceinline__ void finish(const RowAttnArgs& a, long oh0, int nparts, int p,
+                                         int c, int r) {
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      float M = m[h];
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float wgt = fast_exp2(m[h] - M);
+      float lw = l[h] * wgt;
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float ov = o[h][e] * wgt;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
+        o[h][e] = ov;
+      }
+      m[h] = M;
+      l[h] = lw;
+    }
+    if (r != 0) return;
+    T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      const long oh = oh0 + h;
+      if (nparts == 1) {
+        const float inv = 1.f / l[h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) E::store(out + oh * D + c * EPL + e, o[h][e] * inv);
+      } else {
+        float* po = a.ws_o + (oh * a.max_parts + p) * D + c * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<float4*>(po + e) =
+              make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
+        if (c == 0) {
+          a.ws_ml[(oh * a.max_parts + p) * 2] = m[h];
+          a.ws_ml[(oh * a.max_parts + p) * 2 + 1] = l[h];
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ int num_parts(int L, int P) { return L > 0 ? (L + P - 1) / P : 0; }
+
+// ---------------------------------------------------------------- one wave per item
+//
+// BIG: power-of-two blocks of >= 64 tokens (a stage never straddles a block).
+// Otherwise decode stages its partition's block IDs in LDS (one read at the
+// start, so lookups never wait behind the K/V stream) and varlen rows read
+// the table per lane.
 template <typename E, int D, int HG, bool VARLEN, bool BIG>
 __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
+  typedef RowFold<E, D, HG> F;
   typedef typename E::storage T;
-  constexpr int EPL = E::EPL;
-  constexpr int LPR = D / EPL;   // lanes per K/V head row
-  constexpr int RPS = 64 / LPR;  // token rows per load instruction
-  constexpr int SS = 8;          // load steps per pipeline stage
-  constexpr int SUB = SS * RPS;  // tokens per pipeline stage (16..64)
+  constexpr int EPL = F::EPL, LPR = F::LPR, RPS = F::RPS, SS = F::SS, SUB = F::SUB;
+  constexpr int NBUF = kStages;
 
   const int lane = threadIdx.x;
   const int c = lane % LPR;
   const int r = lane / LPR;
 
-  // blockIdx.x = (row * max_parts + p) * Y + y, Y = kv heads * head chunks:
-  // the heads of one partition are adjacent, so they are dispatched together
-  // and read neighbouring bytes of the same token rows.
+  // blockIdx.x = (row * max_parts + p) * Y + y, Y = kv heads * head chunks
   const int Y = a.num_kv_heads * a.head_chunks;
   int x = blockIdx.x;
   const int y = x % Y;
@@ -109,14 +277,13 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     L = min(lk - lq + i + 1, lk);
   }
 
-  T* out = reinterpret_cast<T*>(a.out);
   if (L <= 0) {  // violated precondition: define the output as zeros
     if (p == 0)
       for (int idx = lane; idx < HG * D; idx += 64)
-        E::store(out + ((long)row * a.num_q_heads + h0) * D + idx, 0.f);
+        E::store(reinterpret_cast<T*>(a.out) + ((long)row * a.num_q_heads + h0) * D + idx, 0.f);
     return;
   }
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int nparts = num_parts(L, a.part_tokens);
   if (p >= nparts) return;
   const int tok_begin = p * a.part_tokens;
   const int tok_end = min(L, tok_begin + a.part_tokens);
@@ -137,59 +304,43 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     __syncthreads();
   }
 
-  // Queries of the HG heads, pre-multiplied by scale * log2(e): scores come
-  // out in log2 units and the softmax uses exp2.
-  float qf[HG][EPL];
+  F st;
   {
-    const T* qp =
-        reinterpret_cast<const T*>(a.q) + ((long)row * a.num_q_heads + h0) * D + c * EPL;
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((long)row * a.num_q_heads + h0) * D +
+                  c * EPL;
+    uint4 raw[HG];
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      E::widen(*reinterpret_cast<const uint4*>(qp + h * D), qf[h]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[h][e] *= a.scale_log2;
-    }
+    for (int h = 0; h < HG; ++h) raw[h] = *reinterpret_cast<const uint4*>(qp + h * D);
+    st.set_q(raw, a.scale_log2);
   }
-
-  float m[HG], l[HG], o[HG][EPL];
-#pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-  }
+  st.reset();
 
   const T* kc = reinterpret_cast<const T*>(a.k_cache);
   const T* vc = reinterpret_cast<const T*>(a.v_cache);
-  const int slot_elems = a.num_kv_heads * D;  // elements per token slot
+  const int slot_elems = a.num_kv_heads * D;
   const int head_off = g * D + c * EPL;
+  const unsigned row_bytes = (unsigned)slot_elems * (unsigned)sizeof(T);
   unsigned big_off[BIG ? SS : 1];
   if constexpr (BIG) {
 #pragma unroll
     for (int s = 0; s < SS; ++s)
-      big_off[s] = (unsigned)((s * RPS + r) * slot_elems + c * EPL) * (unsigned)sizeof(T);
+      big_off[s] = (unsigned)(s * RPS + r) * row_bytes + (unsigned)(c * EPL * sizeof(T));
   }
 
-  // Load one stage of SUB tokens.  Lanes past the partition's end read the
-  // last valid token instead (always a written row, never poison) and their
-  // scores are masked, so every load is unconditional and in bounds.
   auto load = [&](uint4 (&kr)[SS], uint4 (&vr)[SS], int t0) {
     const int nvalid = tok_end - t0;  // >= 1
     if constexpr (BIG) {
-      // Wave-uniform base of this stage's rows for head g plus loop-invariant
-      // per-lane byte offsets.  A stage lies inside one block, so rows past
-      // the partition's end are still pool slots of that block (possibly
-      // poison); compute() masks their scores and zeroes their values.
       const int blk = clamp_block(bt[t0 >> bs_log2], nb);
       const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
-      const char* kp = reinterpret_cast<const char*>(kc + base);
-      const char* vp = reinterpret_cast<const char*>(vc + base);
+      const unsigned bytes = (unsigned)min(nvalid, SUB) * row_bytes;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + base, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base, bytes);
 #pragma unroll
-      for (int s = 0; s < SS; ++s) kr[s] = *reinterpret_cast<const uint4*>(kp + big_off[s]);
+      for (int s = 0; s < SS; ++s) kr[s] = buffer_load16(rk, big_off[s]);
 #pragma unroll
-      for (int s = 0; s < SS; ++s) vr[s] = *reinterpret_cast<const uint4*>(vp + big_off[s]);
+      for (int s = 0; s < SS; ++s) vr[s] = buffer_load16(rv, big_off[s]);
     } else {
+      // Rows past the end read the last valid token instead (a written row).
       long off[SS];
 #pragma unroll
       for (int s = 0; s < SS; ++s) {
@@ -213,132 +364,245 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     }
   };
 
-  // Fold one stage into the running (max, sum, output) of this lane's row.
-  auto compute = [&](const uint4 (&kr)[SS], const uint4 (&vr)[SS], int t0) {
-    float sc[HG][SS];
+  // A ring of NBUF register stages: NBUF - 1 stages are in flight while one
+  // is folded in.  Prefetches are unconditional (past the end they re-read
+  // the last stage, which is cached) so the compiler can count outstanding
+  // loads exactly; sched_barrier keeps each prefetch above the fold.
+  uint4 kbuf[NBUF][SS], vbuf[NBUF][SS];
+  const int last_t0 = tok_begin + ((tok_end - tok_begin - 1) / SUB) * SUB;
+  int t0 = tok_begin;
 #pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      float kf[EPL];
-      E::widen(kr[s], kf);
+  for (int i = 0; i < NBUF - 1; ++i) load(kbuf[i], vbuf[i], min(t0 + i * SUB, last_t0));
+  for (;;) {
 #pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[h][e], kf[e], acc);
-        sc[h][s] = acc;
-      }
+    for (int i = 0; i < NBUF; ++i) {
+      load(kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF],
+           min(t0 + (NBUF - 1) * SUB, last_t0));
+      __builtin_amdgcn_sched_barrier(0);
+      st.fold(kbuf[i], vbuf[i], t0, tok_end, r);
+      if (t0 >= last_t0) goto folded;
+      t0 += SUB;
     }
+  }
+folded:
+  st.finish(a, (long)row * a.num_q_heads + h0, nparts, p, c, r);
+}
+
+// ---------------------------------------------------------------- persistent decode
+//
+// Items are ordered (sequence b, head chunk y, partition p), p fastest, so a
+// wave's consecutive items mostly share their query rows.  Wave w owns items
+// [w * n / W, (w + 1) * n / W).
+
+// Sum of x over the wave.
+__device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
-    for (int s = 0; s < SS; ++s)
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
 #pragma unroll
-      for (int h = 0; h < HG; ++h) sc[h][s] = group_sum<LPR>(sc[h][s]);
-    uint4 vz[SS];
-#pragma unroll
-    for (int s = 0; s < SS; ++s) vz[s] = vr[s];
-    if (t0 + SUB > tok_end) {  // last, partial stage: rows past the end do not count
-#pragma unroll
-      for (int s = 0; s < SS; ++s) {
-        const bool valid = t0 + s * RPS + r < tok_end;
-#pragma unroll
-        for (int h = 0; h < HG; ++h) sc[h][s] = valid ? sc[h][s] : -INFINITY;
-        if (!valid) vz[s] = make_uint4(0, 0, 0, 0);
-      }
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+struct ItemCursor {
+  int b, p, y;    // sequence, partition, head chunk
+  int L;          // context length of b
+  int t0, end;    // current stage start, end of the item's tokens
+};
+
+// `lens` is the same array as a.context_lens, passed as a __restrict__
+// kernel argument: the kernel never writes it, so its reads can be scalar
+// loads (counted apart from the K/V stream) rather than vector loads.
+__device__ __forceinline__ int seq_len(const RowAttnArgs& a, const int32_t* __restrict__ lens,
+                                       int b) {
+  return b < a.num_rows ? min(lens[b], a.max_context) : 1;
+}
+
+__device__ __forceinline__ void cursor_begin(ItemCursor& k, int P) {
+  k.t0 = k.p * P;
+  k.end = min(k.L, k.t0 + P);
+}
+
+__device__ __forceinline__ void cursor_next_item(ItemCursor& k, const RowAttnArgs& a,
+                                                 const int32_t* __restrict__ lens, int Y, int P) {
+  if (++k.p * P >= k.L) {
+    k.p = 0;
+    if (++k.y == Y) {
+      k.y = 0;
+      do {
+        ++k.b;
+        k.L = seq_len(a, lens, k.b);
+      } while (k.L <= 0);
     }
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      float mx = sc[h][0];
-#pragma unroll
-      for (int s = 1; s < SS; ++s) mx = fmaxf(mx, sc[h][s]);
-      const float mn = fmaxf(m[h], mx);
-      const float alpha = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      float lsum = l[h] * alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-#pragma unroll
-      for (int s = 0; s < SS; ++s) {
-        const float pr = fast_exp2(sc[h][s] - mn);
-        lsum += pr;
-        sc[h][s] = pr;
+  }
+  cursor_begin(k, P);
+}
+
+template <typename E, int D, int HG>
+__global__ __launch_bounds__(64) void decode_persistent_kernel(
+    RowAttnArgs a, const int32_t* __restrict__ lens, const int32_t* __restrict__ tables) {
+  typedef RowFold<E, D, HG> F;
+  typedef typename E::storage T;
+  constexpr int EPL = F::EPL, LPR = F::LPR, RPS = F::RPS, SS = F::SS, SUB = F::SUB;
+  constexpr int NBUF = kStages;
+
+  const int lane = threadIdx.x;
+  const int c = lane % LPR;
+  const int r = lane / LPR;
+  const int B = a.num_rows;
+  const int P = a.part_tokens;
+  const int Y = a.num_kv_heads * a.head_chunks;
+  const int W = gridDim.x;
+  const int w = blockIdx.x;
+
+  // Total partitions over the batch; wave 0 also zeroes rows whose length
+  // violates the precondition (no item covers them).
+  int total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int L = b < B ? min(lens[b], a.max_context) : 1;
+    if (w == 0 && L <= 0)
+      for (int i = 0; i < a.num_q_heads * D; ++i)
+        E::store(reinterpret_cast<T*>(a.out) + (long)b * a.num_q_heads * D + i, 0.f);
+    total += __builtin_amdgcn_readfirstlane(wave_sum(b < B ? num_parts(L, P) : 0));
+  }
+  const long n_items = (long)total * Y;  // fits: total * Y <= rows * heads * parts
+  const long i0 = n_items * w / W;
+  const long i1 = n_items * (w + 1) / W;
+  int left = (int)(i1 - i0);
+  if (left <= 0) return;
+
+  // Locate the first item: sequence b holds Y * nparts(b) items.
+  ItemCursor cp;
+  {
+    const long target = i0;
+    long acc = 0;
+    cp.b = B;
+    int off = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      const int ni = b < B ? Y * num_parts(min(lens[b], a.max_context), P) : 0;
+      const int incl = wave_scan(ni, lane);
+      const int chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+      if (acc + chunk > target) {
+        const unsigned long long hit = __ballot(acc + incl > target);
+        const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+        const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
+        cp.b = base + l0;
+        off = (int)(target - acc - excl);
+        break;
       }
-      l[h] = lsum;
+      acc += chunk;
     }
+    cp.b = __builtin_amdgcn_readfirstlane(cp.b);
+    if (cp.b >= B) return;  // unreachable when the wave owns items
+    cp.L = seq_len(a, lens, cp.b);
+    const int np = num_parts(cp.L, P);
+    off = __builtin_amdgcn_readfirstlane(off);
+    cp.y = off / np;
+    cp.p = off % np;
+    cursor_begin(cp, P);
+  }
+
+  const T* kc = reinterpret_cast<const T*>(a.k_cache);
+  const T* vc = reinterpret_cast<const T*>(a.v_cache);
+  const int slot_elems = a.num_kv_heads * D;
+  const unsigned row_bytes = (unsigned)slot_elems * (unsigned)sizeof(T);
+  const int bs = a.block_size;
+  const int bs_log2 = a.block_size_log2;
+  const int nb = a.num_blocks;
+  unsigned lane_off[SS];
 #pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      float vf[EPL];
-      E::widen(vz[s], vf);
+  for (int s = 0; s < SS; ++s)
+    lane_off[s] = (unsigned)(s * RPS + r) * row_bytes + (unsigned)(c * EPL * sizeof(T));
+
+  // Query rows of an item's HG heads.
+  auto load_q = [&](uint4 (&raw)[HG], const ItemCursor& k) {
+    const int h0 = (k.y / a.head_chunks) * a.group + (k.y % a.head_chunks) * HG;
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((long)k.b * a.num_q_heads + h0) * D +
+                  c * EPL;
 #pragma unroll
-      for (int h = 0; h < HG; ++h)
+    for (int h = 0; h < HG; ++h) raw[h] = *reinterpret_cast<const uint4*>(qp + h * D);
+  };
+
+  // One stage of the loader's item through a descriptor over its valid rows.
+  auto load = [&](uint4 (&kr)[SS], uint4 (&vr)[SS], const ItemCursor& k) {
+    const int g = k.y / a.head_chunks;
+    const int blk =
+        clamp_block(tables[(long)k.b * a.max_blocks_per_seq + (k.t0 >> bs_log2)], nb);
+    const long base = (((long)blk << bs_log2) + (k.t0 & (bs - 1))) * slot_elems + (long)g * D;
+    const unsigned bytes = (unsigned)min(k.end - k.t0, SUB) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base, bytes);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(sc[h][s], vf[e], o[h][e]);
+    for (int s = 0; s < SS; ++s) kr[s] = buffer_load16(rk, lane_off[s]);
+#pragma unroll
+    for (int s = 0; s < SS; ++s) vr[s] = buffer_load16(rv, lane_off[s]);
+  };
+
+  // The loader runs NBUF - 1 stages ahead of the fold; once its last item's
+  // last stage is issued it keeps re-reading that stage (cached, unused).
+  ItemCursor ld = cp;
+  int ld_left = left;
+  auto ld_advance = [&]() {
+    if (ld.t0 + SUB < ld.end) {
+      ld.t0 += SUB;
+    } else if (ld_left > 1) {
+      --ld_left;
+      cursor_next_item(ld, a, lens, Y, P);
     }
   };
 
-  // Two register stages: the next stage's loads are in flight while the
-  // current one is folded in.  The prefetch is unconditional (at the end it
-  // re-reads the last stage, which is cached) so that the compiler can count
-  // outstanding loads exactly and never waits for the stage in flight.
-  uint4 kA[SS], vA[SS], kB[SS], vB[SS];
-  const int last_t0 = tok_begin + ((tok_end - tok_begin - 1) / SUB) * SUB;
-  int t0 = tok_begin;
-  load(kA, vA, t0);
-  // sched_barrier keeps the scheduler from sinking the prefetch below the
-  // fold of the current stage.
+  F st;
+  {
+    uint4 qraw[HG];
+    load_q(qraw, cp);
+    st.set_q(qraw, a.scale_log2);
+  }
+  st.reset();
+
+  uint4 kbuf[NBUF][SS], vbuf[NBUF][SS];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) {
+    load(kbuf[i], vbuf[i], ld);
+    ld_advance();
+  }
   for (;;) {
-    load(kB, vB, min(t0 + SUB, last_t0));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kA, vA, t0);
-    if (t0 >= last_t0) break;
-    t0 += SUB;
-    load(kA, vA, min(t0 + SUB, last_t0));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kB, vB, t0);
-    if (t0 >= last_t0) break;
-    t0 += SUB;
-  }
-
-  // Merge the RPS independent row states (lanes c, c + LPR, ...).
 #pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float wgt = fast_exp2(m[h] - M);
-    float lw = l[h] * wgt;
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float ov = o[h][e] * wgt;
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
-      o[h][e] = ov;
-    }
-    m[h] = M;
-    l[h] = lw;
-  }
-
-  if (r != 0) return;
-#pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    const long oh = (long)row * a.num_q_heads + h0 + h;
-    if (nparts == 1) {
-      const float inv = 1.f / l[h];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) E::store(out + oh * D + c * EPL + e, o[h][e] * inv);
-    } else {
-      float* po = a.ws_o + (oh * a.max_parts + p) * D + c * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(po + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2],
-                                                         o[h][e + 3]);
-      if (c == 0) {
-        a.ws_ml[(oh * a.max_parts + p) * 2] = m[h];
-        a.ws_ml[(oh * a.max_parts + p) * 2 + 1] = l[h];
+    for (int i = 0; i < NBUF; ++i) {
+      load(kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF], ld);
+      ld_advance();
+      __builtin_amdgcn_sched_barrier(0);
+      st.fold(kbuf[i], vbuf[i], cp.t0, cp.end, r);
+      if (cp.t0 + SUB < cp.end) {
+        cp.t0 += SUB;
+      } else {
+        const int h0 = (cp.y / a.head_chunks) * a.group + (cp.y % a.head_chunks) * HG;
+        st.finish(a, (long)cp.b * a.num_q_heads + h0, num_parts(cp.L, P), cp.p, c, r);
+        if (--left == 0) goto done;
+        const int pb = cp.b, py = cp.y;
+        cursor_next_item(cp, a, lens, Y, P);
+        if (cp.b != pb || cp.y != py) {  // new query rows (about once per wave)
+          uint4 qraw[HG];
+          load_q(qraw, cp);
+          st.set_q(qraw, a.scale_log2);
+        }
+        st.reset();
       }
     }
   }
+done:
+  return;
 }
+
+// ---------------------------------------------------------------- combine
 
 // One block of D threads per (row, query head): rescale the partitions'
 // partial outputs to a common max and normalise.
@@ -348,7 +612,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(RowAttnArgs a) {
   const long oh = blockIdx.x;
   const int row = (int)(oh / a.num_q_heads);
   const int L = min(a.context_lens[row], a.max_context);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int nparts = num_parts(L, a.part_tokens);
   if (nparts <= 1) return;
   const float* ml = a.ws_ml + oh * a.max_parts * 2;
   float M = kNegBig;
@@ -363,6 +627,35 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(RowAttnArgs a) {
   E::store(reinterpret_cast<T*>(a.out) + oh * D + threadIdx.x, acc / lsum);
 }
 
+// ---------------------------------------------------------------- launch
+
+template <typename E, int D, int HG>
+static int launch_persistent(const RowAttnArgs& a, hipStream_t stream) {
+  // One wave per resident slot: CUs x the kernel's occupancy, queried once
+  // per device.
+  static int cached_device = -1, cached_waves = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev != cached_device) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(decode_persistent_kernel<E, D, HG>), 64, 0) !=
+        hipSuccess)
+      return -1;
+    cached_waves = max(1, cus * max(per_cu, 1));
+    cached_device = dev;
+  }
+  const long long max_items =
+      (long long)a.num_rows * a.num_kv_heads * a.head_chunks * a.max_parts;
+  const int waves = (int)min((long long)cached_waves, max_items);
+  if (waves <= 0) return 0;
+  hipLaunchKernelGGL((decode_persistent_kernel<E, D, HG>), dim3(waves), dim3(64), 0, stream, a,
+                     a.context_lens, a.block_tables);
+  return 0;
+}
+
 template <typename E, int D, bool VARLEN, bool BIG>
 static int launch_rows_hg(const RowAttnArgs& a, hipStream_t stream) {
   const long long grid =
@@ -373,10 +666,14 @@ static int launch_rows_hg(const RowAttnArgs& a, hipStream_t stream) {
   switch (a.heads_per_wg) {
 #define PA_HG_CASE(N)                                                                        \
   case N:                                                                                    \
-    if constexpr (N <= (D == 64 ? 8 : 4))                                                    \
-      hipLaunchKernelGGL((row_attn_kernel<E, D, N, VARLEN, BIG>), g, blk, 0, stream, a);     \
-    else                                                                                     \
+    if constexpr (N <= (D == 64 ? 8 : 4)) {                                                  \
+      if constexpr (BIG && !VARLEN)                                                          \
+        return launch_persistent<E, D, N>(a, stream);                                        \
+      else                                                                                   \
+        hipLaunchKernelGGL((row_attn_kernel<E, D, N, VARLEN, BIG>), g, blk, 0, stream, a);   \
+    } else {                                                                                 \
       return -1;                                                                             \
+    }                                                                                        \
     break;
     PA_HG_CASE(1)
     PA_HG_CASE(2)
