@@ -11,8 +11,8 @@
 // Tiling.  A workgroup (4 waves) owns one KV head, HPW of its query heads and
 // BMQ = 32 * (4 / HPW) consecutive query rows; each wave owns 32 rows of one
 // head.  Key/value tiles of 64 tokens are gathered through the block table
-// into LDS once per workgroup and shared by all four waves.  Per tile a wave
-// computes
+// into LDS once per workgroup (double-buffered) and shared by all four waves.
+// Per tile a wave computes
 //     S^T (64 keys x 32 rows)  = K_tile . Q^T       (v_mfma_f32_32x32x16_bf16)
 //     O^T (D x 32 rows)       += V_tile^T . P^T
 // Computing the transposed products puts each query row in one lane (and its
@@ -21,8 +21,18 @@
 // a permuted order (bits 2 and 3 of the row index swapped) so that the fp32
 // scores a lane receives are exactly the 8-consecutive-key runs that the
 // second MFMA expects as its B operand: P goes from the score registers to
-// the PV product without touching LDS.  V is stored transposed in LDS (head
-// dim major) because the PV product reduces over keys.
+// the PV product without touching LDS.  V stays row-major in LDS; its
+// transposed operand (8 consecutive keys of one head-dim column per lane) is
+// read with the gfx950 LDS transpose load (ds_read_b64_tr_b16), two per
+// operand.
+//
+// LDS layouts (row strides chosen for conflict-free access):
+//   K: row stride D + 8 elements -- consecutive rows shift by 16 bytes, so
+//      the 16 lanes of an operand read (16 different rows, same column) hit
+//      16 different 16-byte bank groups;
+//   V: row stride D + 32 elements -- consecutive rows shift by a quarter of
+//      the 256-byte bank space, so the 4 keys x 64 bytes of a transpose read
+//      cover all banks once.
 //
 // Work order: the grid runs the last (heaviest, under the causal mask) query
 // tiles of every sequence first.  Tiles entirely above the diagonal are
@@ -32,11 +42,26 @@
 
 namespace pa {
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 __device__ __forceinline__ int swap_bits_2_3(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <int D, int HPW>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefill_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// LDS transpose read: within each 16-lane group, lane j points at 4
+// consecutive 16-bit elements (chunk j); lane i receives element
+// chunk[4k + i/4][i%4] as its k-th value.
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+template <int D, int HPW, bool BIG>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BN = 64;             // keys per tile
   constexpr int WPH = 4 / HPW;       // waves per query head
@@ -44,12 +69,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int KC = D / 16;         // k-steps of the QK^T product
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int KS = D + 8;          // LDS row stride of K (elements)
-  constexpr int VS = BN + 8;         // LDS row stride of V^T (elements)
+  constexpr int VS = D + 32;         // LDS row stride of V (elements)
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   constexpr int CPT = BN * CPR / 256;  // chunks per thread per tile
+  constexpr int RPI = 256 / CPR;     // tile rows covered per chunk index i
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,45 +131,63 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
   const int32_t* bt = a.block_tables + (long)b * a.max_blocks_per_seq;
-  const long slot_elems = (long)a.num_kv_heads * D;
+  const int slot_elems = a.num_kv_heads * D;
+  const unsigned row_bytes = (unsigned)slot_elems * 2u;
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nblk = a.num_blocks;
 
+  // Tile chunk i of this thread: row tid / CPR + RPI * i, 16-byte column tid % CPR.
+  const int trow = tid / CPR;
+  const int tcol = tid % CPR;
+  unsigned big_off[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    big_off[i] = (unsigned)(trow + RPI * i) * row_bytes + (unsigned)(tcol * 16);
+
   uint4 kreg[CPT], vreg[CPT];
   auto load_tile = [&](int kt) {
+    const int t0 = kt * BN;
+    if constexpr (BIG) {
+      // The 64-key tile lies in one block; rows past Lk fall outside the
+      // descriptor and read zero.
+      const int blk = clamp_block(bt[t0 >> bs_log2], nblk);
+      const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
+      const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
+      const __amdgpu_buffer_rsrc_t rk = prefill_rsrc(kcache + base, bytes);
+      const __amdgpu_buffer_rsrc_t rv = prefill_rsrc(vcache + base, bytes);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / CPR;
-      const int dc = ci % CPR;
-      const int j = kt * BN + key;
-      if (j < Lk) {
-        long slot;
-        if (bs_log2 >= 0)
-          slot = ((long)clamp_block(bt[j >> bs_log2], nblk) << bs_log2) + (j & (bs - 1));
-        else
-          slot = (long)clamp_block(bt[j / bs], nblk) * bs + j % bs;
-        const long off = slot * slot_elems + (long)g * D + dc * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(kcache + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(vcache + off);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < CPT; ++i)
+        kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, big_off[i], 0, 0));
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, big_off[i], 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int j = t0 + trow + RPI * i;
+        if (j < Lk) {
+          long slot;
+          if (bs_log2 >= 0)
+            slot = ((long)clamp_block(bt[j >> bs_log2], nblk) << bs_log2) + (j & (bs - 1));
+          else
+            slot = (long)clamp_block(bt[j / bs], nblk) * bs + j % bs;
+          const long off = slot * slot_elems + (long)g * D + tcol * 8;
+          kreg[i] = *reinterpret_cast<const uint4*>(kcache + off);
+          vreg[i] = *reinterpret_cast<const uint4*>(vcache + off);
+        } else {
+          kreg[i] = make_uint4(0, 0, 0, 0);
+          vreg[i] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / CPR;
-      const int dc = ci % CPR;
-      *reinterpret_cast<uint4*>(&sK[key * KS + dc * 8]) = kreg[i];
-      const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sVt[(dc * 8 + e) * VS + key] = (uint16_t)((e & 1) ? (wv[e >> 1] >> 16) : wv[e >> 1]);
+      const int row = trow + RPI * i;
+      *reinterpret_cast<uint4*>(&sK[buf][row * KS + tcol * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[buf][row * VS + tcol * 8]) = vreg[i];
     }
   };
 
@@ -155,18 +199,24 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   const int my_row = row0 + lr;
   const int klim = delta + my_row;  // last key this lane's row may see
   const int krow_perm = swap_bits_2_3(lr);
+  // Transpose-read address pieces: 16-lane group q = lane / 16 covers head-dim
+  // columns 16 * (q % 2) .. + 15 of keys 8 * (q / 2) + 4 * half + 0..3.
+  const int tr_j = lane & 15;
+  const int tr_key = 8 * lh + tr_j / 4;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
 
   load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) load_tile(1);
+  __syncthreads();
   for (int kt = 0; kt < n_tiles; ++kt) {
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    const int buf = kt & 1;
     if (wave_active && kt * BN <= kmax_wave) {
       f32x16 sacc[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         sacc[nb] = f32x16{};
-        const uint16_t* kp = &sK[(nb * 32 + krow_perm) * KS + lh * 8];
+        const uint16_t* kp = &sK[buf][(nb * 32 + krow_perm) * KS + lh * 8];
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
           const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
@@ -214,14 +264,21 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vp = &sVt[(db * 32 + lr) * VS + lh * 8];
+      for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(vp + kc * 16);
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* vp = &sV[buf][(kc * 16 + tr_key) * VS + db * 32 + tr_col];
+          const bf16x4 lo = lds_read_tr(vp);
+          const bf16x4 hi = lds_read_tr(vp + 4 * VS);
+          const bf16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pB[kc], oacc[db], 0, 0, 0);
         }
       }
+    }
+    // Stage the prefetched tile into the other buffer, then fetch the next.
+    if (kt + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      if (kt + 2 < n_tiles) load_tile(kt + 2);
     }
     __syncthreads();
   }
@@ -254,8 +311,12 @@ static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
       n_qt * a.num_seqs * (long long)a.num_kv_heads * (a.group / HPW);
   if (grid <= 0) return 0;
   if (grid > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     a);
+  if (a.block_size_log2 >= 6)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, a);
   return 0;
 }
 
