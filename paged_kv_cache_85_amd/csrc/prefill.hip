@@ -62,7 +62,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
 }
 
 template <int D, int HPW, bool BIG>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BN = 64;             // keys per tile
   constexpr int WPH = 4 / HPW;       // waves per query head
   constexpr int BMQ = 32 * WPH;      // query rows per workgroup
