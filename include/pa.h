@@ -43,6 +43,7 @@
  *     result is then unspecified.  With the environment variable PA_CHECK=1
  *     the library copies the index arrays to the host, validates them and
  *     returns PA_E_INVAL on a violation (this synchronises the stream).
+ *   - scale (the softmax temperature applied to q.k) must be finite and > 0.
  *   - Outputs must not alias inputs; k/v must not alias the pools.
  *   - The library is stateless; calls on different streams may overlap.
  */

@@ -130,7 +130,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
               void* stream) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
-      block_size < 1 || max_blocks_per_seq < 1 || max_context_len < 1 || !isfinite(scale))
+      block_size < 1 || max_blocks_per_seq < 1 || max_context_len < 1 || !isfinite(scale) ||
+      !(scale > 0.f))
     return PA_E_INVAL;
   if (num_q_heads % num_kv_heads) return PA_E_INVAL;
   if (head_dim != 64 && head_dim != 128) return PA_E_UNSUPPORTED;
@@ -206,7 +207,7 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
                       int32_t dtype, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
       num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 || block_size < 1 ||
-      max_blocks_per_seq < 1 || !isfinite(scale))
+      max_blocks_per_seq < 1 || !isfinite(scale) || !(scale > 0.f))
     return PA_E_INVAL;
   if (num_q_heads % num_kv_heads) return PA_E_INVAL;
   if (head_dim != 64 && head_dim != 128) return PA_E_UNSUPPORTED;

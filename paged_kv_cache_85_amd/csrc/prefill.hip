@@ -223,27 +223,38 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qB[kk], sacc[nb], 0, 0, 0);
         }
       }
-      // Lane (row lr, half lh) holds, in item t of block nb, the score of key
-      // kt*64 + nb*32 + 16*(t/8) + 8*lh + t%8.
+      // Lane (row lr, half lh) holds, in item t of block nb, the raw score of
+      // key kt*64 + nb*32 + 16*(t/8) + 8*lh + t%8.
       const bool need_mask = (kt * BN + BN - 1 > delta + row0) || (kt * BN + BN > Lk);
-      float mx = kNegBig;
+      if (need_mask) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          float s = sacc[nb][t] * a.scale_log2;
-          if (need_mask) {
+          for (int t = 0; t < 16; ++t) {
             const int key = kt * BN + nb * 32 + 16 * (t >> 3) + 8 * lh + (t & 7);
-            if (key > klim || key >= Lk) s = -INFINITY;
+            if (key > klim || key >= Lk) sacc[nb][t] = -INFINITY;
           }
-          sacc[nb][t] = s;
-          mx = fmaxf(mx, s);
-        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - mn);
-      m_run = mn;
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mx = fmaxf(mx, sacc[nb][t]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;  // scale > 0: max commutes with it
+      // Lazy rescale: the reference max m_run only moves when a row's max
+      // exceeds it by more than 2^8 (so probabilities stay <= 256); the final
+      // O / l is the same for any reference, and the 64 multiplies of the O
+      // rescale are skipped for every tile that does not move it.
+      if (__any(mx > m_run + 8.f)) {
+        const float mn = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+      }
       float psum = 0.f;
       bf16x8 pB[4];
 #pragma unroll
@@ -252,17 +263,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int half = 0; half < 2; ++half) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pr = fast_exp2(sacc[nb][half * 8 + e] - mn);
+            const float pr = fast_exp2(fmaf(sacc[nb][half * 8 + e], a.scale_log2, -m_run));
             psum += pr;
             pB[nb * 2 + half][e] = (__bf16)pr;
           }
         }
       }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+      l_run += psum;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll

@@ -72,6 +72,8 @@ def test_decode_validation(lib):
     assert _decode(lib, bs=0) == pa.PA_E_INVAL
     assert _decode(lib, maxl=200, mb=8, bs=16) == pa.PA_E_INVAL     # table too short
     assert _decode(lib, scale=float("nan")) == pa.PA_E_INVAL
+    assert _decode(lib, scale=0.0) == pa.PA_E_INVAL                # scale must be > 0
+    assert _decode(lib, scale=-0.125) == pa.PA_E_INVAL
     assert _decode(lib, maxl=1000, mb=64, ws=None) == pa.PA_E_WORKSPACE
     assert _decode(lib, maxl=1000, mb=64, ws=FAKE, wsb=16) == pa.PA_E_WORKSPACE
     assert _decode(lib, B=0) == pa.PA_OK                           # empty batch: no-op
@@ -92,6 +94,7 @@ def test_prefill_validation(lib):
     assert _prefill(lib, mq=50, mk=40) == pa.PA_E_INVAL            # Lq may not exceed Lk
     assert _prefill(lib, mk=100, mb=4, bs=16) == pa.PA_E_INVAL      # table too short
     assert _prefill(lib, cq=None) == pa.PA_E_INVAL
+    assert _prefill(lib, scale=-1.0) == pa.PA_E_INVAL
     assert _prefill(lib, tq=0) == pa.PA_OK
     assert _prefill(lib, B=0) == pa.PA_OK
 
