@@ -70,10 +70,12 @@ def prefill_bytes(case) -> int:
     return qo + 2 * keys * case.num_kv_heads * case.head_dim * e
 
 
-def kernel_sources_digest() -> str:
+def kernel_sources_digest(files=None) -> str:
+    """Digest of the kernel sources a measurement depends on (all of csrc/ by
+    default), so that a counter summary taken on other sources is not used."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_85_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -81,7 +83,7 @@ def kernel_sources_digest() -> str:
 
 def measured_traffic(name: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current sources of the kernels it covers; else None."""
     path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -91,11 +93,12 @@ def measured_traffic(name: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.strip().split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources") != kernel_sources_digest():
-        return None
+    files = [x.strip() for x in kv.get("sources", "").split(",") if x.strip()]
     try:
+        if kv.get("kernel_sources") != kernel_sources_digest(files or None):
+            return None
         return int(float(kv["bytes_per_launch"]))
-    except (KeyError, ValueError):
+    except (KeyError, ValueError, OSError):
         return None
 
 
@@ -133,12 +136,31 @@ def cpu_oracle_baseline(dec, pre4):
     }
 
 
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(torch, dev) -> None:
+    """A plain copy of known size (1 GiB read, 1 GiB written per launch), run
+    under the same counters as the path so that their bytes can be scaled."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 x {COPY_PROBE_BYTES} B read + written")
+    del src, dst
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a 1 GiB elementwise copy three times: "
+                         "the known-size kernel that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
@@ -300,6 +322,8 @@ def main() -> int:
         cpu = cpu_oracle_baseline(dec, pre4)
         result["cpu_baseline"] = cpu["decode"]
         result["cpu_baseline_prefill"] = cpu["prefill"]
+    if args.copy_probe:
+        copy_probe(torch, dev)
     print(json.dumps(result), flush=True)
     return 0
 
