@@ -10,10 +10,10 @@
 //
 // Tiling.  A workgroup (4 waves) owns one KV head, HPW of its query heads and
 // BMQ = 32 * (4 / HPW) consecutive query rows; each wave owns 32 rows of one
-// head.  Key/value tiles of 64 tokens are gathered through the block table
-// into LDS once per workgroup (double-buffered) and shared by all four waves.
-// Per tile a wave computes
-//     S^T (64 keys x 32 rows)  = K_tile . Q^T       (v_mfma_f32_32x32x16_bf16)
+// head.  Key/value tiles of 32 tokens are gathered through the block table
+// into LDS once per workgroup and shared by the four waves.  Per tile a wave
+// computes
+//     S^T (32 keys x 32 rows)  = K_tile . Q^T       (v_mfma_f32_32x32x16_bf16)
 //     O^T (D x 32 rows)       += V_tile^T . P^T
 // Computing the transposed products puts each query row in one lane (and its
 // mirror lane 32 apart), so the row max / row sum of the online softmax are
@@ -26,17 +26,26 @@
 // read with the gfx950 LDS transpose load (ds_read_b64_tr_b16), two per
 // operand.
 //
-// LDS layouts (row strides chosen for conflict-free access):
-//   K: row stride D + 8 elements -- consecutive rows shift by 16 bytes, so
-//      the 16 lanes of an operand read (16 different rows, same column) hit
-//      16 different 16-byte bank groups;
-//   V: row stride D + 32 elements -- consecutive rows shift by a quarter of
-//      the 256-byte bank space, so the 4 keys x 64 bytes of a transpose read
-//      cover all banks once.
+// Tile ring.  LDS holds three tile stages; tile kt + 2 is requested while tile
+// kt is computed, and one barrier per tile both publishes the arrived tile
+// and frees the stage the next request overwrites.  When a block holds whole
+// tiles (power-of-two block size >= 32) the tiles travel from HBM straight
+// into LDS (buffer loads with the LDS-destination bit: no register staging,
+// no LDS store instructions); other block sizes look every row up on its own
+// and pass it through registers.  Both loaders fill the same layout, so the
+// arithmetic -- and the result, bit for bit -- does not depend on the block
+// size.
+//
+// LDS rows are unpadded (D elements) and XOR-swizzled at 16-byte granularity:
+// logical chunk c of row r sits at physical chunk c ^ swz(r), with swz chosen
+// so that the 16 rows of an operand read and the 4 keys x 4 chunks of a
+// transpose read each touch all 64 banks once.
 //
 // Work order: the grid runs the last (heaviest, under the causal mask) query
 // tiles of every sequence first.  Tiles entirely above the diagonal are
 // skipped; masking is applied only to tiles that cross it.
+#include <type_traits>
+
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -49,9 +58,40 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefill_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+#ifndef PA_PREFILL_OCC
+#define PA_PREFILL_OCC 2
+#endif
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, no stride, num_records = bytes) in scalar
+// registers; offsets at or past `bytes` read zero.
+__device__ __forceinline__ u32x4 stream_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)p),
+               (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu),
+               (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS: the wave's 64
+// lanes fill 1 KiB at dst (wave-uniform) in lane order.  Issued as inline
+// assembly so that the compiler does not add its own waits for it; the
+// caller orders it with vm_wait and barriers.
+__device__ __forceinline__ void lds_load16(u32x4 rsrc, uint16_t* dst, unsigned voff) {
+  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Wait until at most N vector-memory loads of this thread are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // LDS transpose read: within each 16-lane group, lane j points at 4
@@ -61,133 +101,241 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-template <int D, int HPW, bool BIG>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int BN = 64;             // keys per tile
-  constexpr int WPH = 4 / HPW;       // waves per query head
-  constexpr int BMQ = 32 * WPH;      // query rows per workgroup
-  constexpr int KC = D / 16;         // k-steps of the QK^T product
-  constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int KS = D + 8;          // LDS row stride of K (elements)
-  constexpr int VS = D + 32;         // LDS row stride of V (elements)
-  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-  constexpr int CPT = BN * CPR / 256;  // chunks per thread per tile
-  constexpr int RPI = 256 / CPR;     // tile rows covered per chunk index i
+// Physical 16-byte chunk of logical chunk c in tile row r is c ^ tile_swz(r).
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * VS];
+#ifndef PA_PREFILL_BN
+#define PA_PREFILL_BN 32
+#endif
+#ifndef PA_PREFILL_NST
+#define PA_PREFILL_NST 3
+#endif
+#ifndef PA_PREFILL_SPLIT
+#define PA_PREFILL_SPLIT 0
+#endif
+
+// Wait until at most `tiles` tile requests of NI16 16-byte loads each are
+// still in flight (0 <= tiles <= MAXT).
+template <int PER_TILE, int MAXT>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  if constexpr (MAXT > 0) {
+    if (tiles >= MAXT) {
+      vm_wait<MAXT * PER_TILE>();
+      return;
+    }
+    wait_tiles<PER_TILE, MAXT - 1>(tiles);
+  } else {
+    vm_wait<0>();
+  }
+}
+
+// Persistent launches keep one 16-bit tile count per sequence in LDS.
+constexpr int kMaxPersistSeqs = 2048;
+
+// Position of a walk over the heavy-first item list, in chunks of 64
+// sequences of one query-tile index: chunk (qt_rev, b0) starts at rank kbase
+// among the non-empty items.
+struct ItemWalk {
+  int qt_rev;
+  int b0;
+  int kbase;
+};
+
+// Advance the walk to the non-empty item of rank k (k never decreases between
+// calls); false once the list is exhausted.  Wave-uniform.
+__device__ __forceinline__ bool walk_to(ItemWalk& wk, int k, const uint16_t* ntiles,
+                                        int num_seqs, int n_qt, int inner, int lane, int& qt,
+                                        int& b, int& gh) {
+  while (wk.qt_rev < n_qt) {
+    const int q = n_qt - 1 - wk.qt_rev;
+    const int bb = wk.b0 + lane;
+    const bool v = bb < num_seqs && (int)ntiles[bb] > q;
+    const unsigned long long m = __ballot(v);
+    const int cnt = __popcll(m) * inner;
+    if (k < wk.kbase + cnt) {
+      const int t = k - wk.kbase;
+      const int s = t / inner;
+      gh = t - s * inner;
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+      const unsigned long long sel = __ballot(v && below == s);
+      b = wk.b0 + __builtin_ctzll(sel);
+      qt = q;
+      return true;
+    }
+    wk.kbase += cnt;
+    wk.b0 += 64;
+    if (wk.b0 >= num_seqs) {
+      wk.b0 = 0;
+      ++wk.qt_rev;
+    }
+  }
+  return false;
+}
+
+// BN keys per tile, NST tile stages in LDS.
+template <int D, int HPW, bool DMA, int BN, int NST>
+__global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
+    PrefillArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k) {
+  constexpr int NB = BN / 32;                // 32-key score blocks per tile
+  constexpr int WPH = 4 / HPW;
+  constexpr int BMQ = 32 * WPH;
+  constexpr int KC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NI = BN * CPR / 256;         // loads per thread per tensor per tile
+  constexpr int SPLIT = (NB == 1 && PA_PREFILL_SPLIT) ? 2 : 1;
+  static_assert(NST >= 2 && NST <= 4, "stage count");
+
+  // Stage s: K rows [0, BN*D), then V rows.
+  __shared__ __attribute__((aligned(16))) uint16_t st[NST][2 * BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
+  const int num_seqs = a.num_seqs;
   const int hchunks = a.group / HPW;
   const int inner = a.num_kv_heads * hchunks;
-  int x = blockIdx.x;
-  const int gh = x % inner;
-  x /= inner;
-  const int b = x % a.num_seqs;
-  const int qt_rev = x / a.num_seqs;
   const int n_qt = (a.max_seqlen_q + BMQ - 1) / BMQ;
-  const int qt = n_qt - 1 - qt_rev;
+
+  // Work items, heaviest first: item ((qt_rev * num_seqs) + b) * inner + gh
+  // is query tile n_qt - 1 - qt_rev of sequence b, KV head / head chunk gh;
+  // tiles past a sequence's end are empty.  A launch with one workgroup per
+  // item maps blockIdx to its item.  A persistent launch (one workgroup per
+  // resident slot) walks the non-empty items in that order and takes those
+  // whose rank k among them is r * G + i (r even) or r * G + G - 1 - i (r odd)
+  // for workgroup i of G: a snake over a list sorted by decreasing cost,
+  // which evens out the total work per workgroup.
+  __shared__ uint16_t s_ntiles[kMaxPersistSeqs];
+  const bool persistent = a.persistent != 0;
+  if (persistent) {
+    for (int i = tid; i < num_seqs; i += 256) {
+      const int qs = cu_q[i], qe = cu_q[i + 1], kl = cu_k[i + 1] - cu_k[i];
+      int nq = 0;
+      if (qs >= 0 && qs < a.total_q) {
+        const int lk = min(min(kl, a.max_seqlen_k), a.max_blocks_per_seq * a.block_size);
+        const int lq = min(min(min(qe - qs, a.max_seqlen_q), lk), a.total_q - qs);
+        nq = lq > 0 ? (lq + BMQ - 1) / BMQ : 0;
+      }
+      s_ntiles[i] = (uint16_t)nq;
+    }
+    __syncthreads();
+  }
+  ItemWalk walk{0, 0, 0};
+  const int G = gridDim.x;
+  const int gi = blockIdx.x;
+
+  for (int round = 0;; ++round) {
+  int qt, b, gh;
+  if (persistent) {
+    const int k = round * G + ((round & 1) ? G - 1 - gi : gi);
+    if (!walk_to(walk, k, s_ntiles, num_seqs, n_qt, inner, lane, qt, b, gh)) break;
+  } else {
+    if (round > 0) break;
+    int x = gi;
+    gh = x % inner;
+    x /= inner;
+    b = x % num_seqs;
+    qt = n_qt - 1 - x / num_seqs;
+  }
   const int g = gh / hchunks;
   const int hc = gh % hchunks;
 
-  const int q_start = a.cu_seqlens_q[b];
-  if (q_start < 0 || q_start >= a.total_q) return;
-  const int Lk = min(min(a.cu_seqlens_k[b + 1] - a.cu_seqlens_k[b], a.max_seqlen_k),
-                     a.max_blocks_per_seq * a.block_size);
-  const int Lq = min(min(min(a.cu_seqlens_q[b + 1] - q_start, a.max_seqlen_q), Lk),
-                     a.total_q - q_start);
-  if (qt < 0 || qt * BMQ >= Lq) return;
+  // Sequence bounds: scalar loads (restrict, uniform address), kept uniform.
+  const int q_start = __builtin_amdgcn_readfirstlane(cu_q[b]);
+  const int q_end = __builtin_amdgcn_readfirstlane(cu_q[b + 1]);
+  const int k_len = __builtin_amdgcn_readfirstlane(cu_k[b + 1] - cu_k[b]);
+  if (q_start < 0 || q_start >= a.total_q) continue;
+  const int Lk = min(min(k_len, a.max_seqlen_k), a.max_blocks_per_seq * a.block_size);
+  const int Lq = min(min(min(q_end - q_start, a.max_seqlen_q), Lk), a.total_q - q_start);
+  if (qt < 0 || qt * BMQ >= Lq) continue;
   const int delta = Lk - Lq;
+  const float scale_log2 = a.scale_log2;
+  const int num_q_heads = a.num_q_heads;
 
   const int head_local = w / WPH;
   const int h = g * a.group + hc * HPW + head_local;
-  const int row0 = qt * BMQ + (w % WPH) * 32;  // first row of this wave in the sequence
+  const int row0 = qt * BMQ + (w % WPH) * 32;
   const bool wave_active = row0 < Lq;
   const int kmax_wave = delta + min(row0 + 32, Lq) - 1;
   const int kmax_wg = delta + min(qt * BMQ + BMQ, Lq) - 1;
   const int n_tiles = kmax_wg / BN + 1;
 
-  // Q rows of this wave: B operand of S^T = K Q^T (lane holds 8 consecutive
-  // head-dim elements of row lr for each 16-wide k-step).
   bf16x8 qB[KC];
-  {
-    const int qrow = row0 + lr;
-    if (wave_active && qrow < Lq) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((long)(q_start + qrow) * a.num_q_heads + h) * D + lh * 8;
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) qB[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) qB[kk] = bf16x8{};
-    }
-  }
-
   const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
-  const int32_t* bt = a.block_tables + (long)b * a.max_blocks_per_seq;
+  const int32_t* bt = tables + (long)b * a.max_blocks_per_seq;
   const int slot_elems = a.num_kv_heads * D;
   const unsigned row_bytes = (unsigned)slot_elems * 2u;
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nblk = a.num_blocks;
 
-  // Tile chunk i of this thread: row tid / CPR + RPI * i, 16-byte column tid % CPR.
-  const int trow = tid / CPR;
-  const int tcol = tid % CPR;
-  unsigned big_off[CPT];
+  // Load i of this wave fills physical chunks [(w * NI + i) * 64, +64) of a
+  // tile: row s / CPR, physical chunk s % CPR, which holds logical chunk
+  // (s % CPR) ^ swz(row).
+  unsigned src_off[NI];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    big_off[i] = (unsigned)(trow + RPI * i) * row_bytes + (unsigned)(tcol * 16);
+  for (int i = 0; i < NI; ++i) {
+    const int s = (w * NI + i) * 64 + lane;
+    const int r = s / CPR;
+    const int c = (s % CPR) ^ tile_swz<D>(r);
+    src_off[i] = (unsigned)r * row_bytes + (unsigned)(c * 16);
+  }
 
-  uint4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int kt) {
+  // Request tile kt, which lies in physical block blk_id, into stage buffers
+  // (dk, dv).  Rows past Lk lie outside the descriptors and arrive as zeros.
+  auto request = [&](uint16_t* dk, uint16_t* dv, int kt, int blk_id) __attribute__((always_inline)) {
     const int t0 = kt * BN;
-    if constexpr (BIG) {
-      // The 64-key tile lies in one block; rows past Lk fall outside the
-      // descriptor and read zero.
-      const int blk = clamp_block(bt[t0 >> bs_log2], nblk);
-      const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
-      const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
-      const __amdgpu_buffer_rsrc_t rk = prefill_rsrc(kcache + base, bytes);
-      const __amdgpu_buffer_rsrc_t rv = prefill_rsrc(vcache + base, bytes);
+    const int blk = clamp_block(blk_id, nblk);
+    const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
+    const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
+    const u32x4 rk = stream_rsrc(kcache + base, bytes);
+    const u32x4 rv = stream_rsrc(vcache + base, bytes);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, big_off[i], 0, 0));
+    for (int i = 0; i < NI; ++i) lds_load16(rk, dk + (w * NI + i) * 512, src_off[i]);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, big_off[i], 0, 0));
-    } else {
+    for (int i = 0; i < NI; ++i) lds_load16(rv, dv + (w * NI + i) * 512, src_off[i]);
+  };
+
+  // Other block sizes: the same chunks through registers, each row looked up
+  // in the block table on its own, then written to the same LDS positions.
+  uint4 kreg[NI], vreg[NI];
+  auto fetch = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int j = t0 + trow + RPI * i;
-        if (j < Lk) {
-          long slot;
-          if (bs_log2 >= 0)
-            slot = ((long)clamp_block(bt[j >> bs_log2], nblk) << bs_log2) + (j & (bs - 1));
-          else
-            slot = (long)clamp_block(bt[j / bs], nblk) * bs + j % bs;
-          const long off = slot * slot_elems + (long)g * D + tcol * 8;
-          kreg[i] = *reinterpret_cast<const uint4*>(kcache + off);
-          vreg[i] = *reinterpret_cast<const uint4*>(vcache + off);
-        } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < NI; ++i) {
+      const int s = (w * NI + i) * 64 + lane;
+      const int j = kt * BN + s / CPR;
+      if (j < Lk) {
+        long slot;
+        if (bs_log2 >= 0)
+          slot = ((long)clamp_block(bt[j >> bs_log2], nblk) << bs_log2) + (j & (bs - 1));
+        else
+          slot = (long)clamp_block(bt[j / bs], nblk) * bs + j % bs;
+        const int c = (s % CPR) ^ tile_swz<D>(s / CPR);
+        const long off = slot * slot_elems + (long)g * D + c * 8;
+        kreg[i] = *reinterpret_cast<const uint4*>(kcache + off);
+        vreg[i] = *reinterpret_cast<const uint4*>(vcache + off);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto deposit = [&](uint16_t* dk, uint16_t* dv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int row = trow + RPI * i;
-      *reinterpret_cast<uint4*>(&sK[buf][row * KS + tcol * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[buf][row * VS + tcol * 8]) = vreg[i];
+    for (int i = 0; i < NI; ++i) {
+      const int s = (w * NI + i) * 64 + lane;
+      *reinterpret_cast<uint4*>(dk + s * 8) = kreg[i];
+      *reinterpret_cast<uint4*>(dv + s * 8) = vreg[i];
     }
   };
 
@@ -197,105 +345,191 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   float m_run = kNegBig;
   float l_run = 0.f;
   const int my_row = row0 + lr;
-  const int klim = delta + my_row;  // last key this lane's row may see
-  const int krow_perm = swap_bits_2_3(lr);
-  // Transpose-read address pieces: 16-lane group q = lane / 16 covers head-dim
-  // columns 16 * (q % 2) .. + 15 of keys 8 * (q / 2) + 4 * half + 0..3.
+  const int klim = delta + my_row;
+  // K operand: lane reads tile row 32 * nb + krow (bits 2 and 3 of lr
+  // swapped) at logical chunk 2 * kk + lh.
+  const int krow = swap_bits_2_3(lr);
+  const int kswz = tile_swz<D>(krow);
+  // V transpose operand: lane reads key 16 * kc + 8 * lh + 4 * half + j / 4,
+  // elements 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3) .. + 3.
   const int tr_j = lane & 15;
   const int tr_key = 8 * lh + tr_j / 4;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+  const int tr_el = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
 
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) load_tile(1);
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (wave_active && kt * BN <= kmax_wave) {
-      f32x16 sacc[2];
+  auto compute = [&](const uint16_t* sk, const uint16_t* sv, int kt) __attribute__((always_inline)) {
+    f32x16 sacc[NB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        sacc[nb] = f32x16{};
-        const uint16_t* kp = &sK[buf][(nb * 32 + krow_perm) * KS + lh * 8];
+    for (int nb = 0; nb < NB; ++nb) {
+      // (tile_swz of rows 32 * nb + krow equals that of krow: it only reads
+      // the low four bits of the row.)
+      if constexpr (SPLIT == 2) {
+        f32x16 s2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+          const int pc = (2 * kk + lh) ^ kswz;
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(sk + (nb * 32 + krow) * D + pc * 8);
+          s2[kk & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qB[kk], s2[kk & 1], 0, 0, 0);
+        }
+        sacc[nb] = s2[0] + s2[1];
+      } else {
+        sacc[nb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          const int pc = (2 * kk + lh) ^ kswz;
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(sk + (nb * 32 + krow) * D + pc * 8);
           sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qB[kk], sacc[nb], 0, 0, 0);
         }
       }
-      // Lane (row lr, half lh) holds, in item t of block nb, the raw score of
-      // key kt*64 + nb*32 + 16*(t/8) + 8*lh + t%8.
-      const bool need_mask = (kt * BN + BN - 1 > delta + row0) || (kt * BN + BN > Lk);
-      if (need_mask) {
+    }
+    // Item t of block nb holds the raw score of key
+    // kt*BN + 32*nb + 16*(t/8) + 8*lh + t%8.
+    const bool need_mask = (kt * BN + BN - 1 > delta + row0) || (kt * BN + BN > Lk);
+    if (need_mask) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int key = kt * BN + nb * 32 + 16 * (t >> 3) + 8 * lh + (t & 7);
-            if (key > klim || key >= Lk) sacc[nb][t] = -INFINITY;
-          }
+        for (int t = 0; t < 16; ++t) {
+          const int key = kt * BN + 32 * nb + 16 * (t >> 3) + 8 * lh + (t & 7);
+          if (key > klim || key >= Lk) sacc[nb][t] = -INFINITY;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, sacc[nb][t]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0: max commutes with it
+    // Lazy rescale: the reference max m_run only moves when a row's max
+    // exceeds it by more than 2^8 (so probabilities stay <= 256); the final
+    // O / l is the same for any reference, and the O rescale is skipped for
+    // every tile that does not move it.
+    if (__any(mx > m_run + 8.f)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+    }
+    float psum = 0.f;
+    bf16x8 pB[2 * NB];
+#pragma unroll
+    for (int kc = 0; kc < 2 * NB; ++kc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = fast_exp2(fmaf(sacc[kc >> 1][(kc & 1) * 8 + e], scale_log2, -m_run));
+        psum += pr;
+        pB[kc][e] = (__bf16)pr;
       }
-      float mx = sacc[0][0];
+    }
+    l_run += psum;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+    for (int kc = 0; kc < 2 * NB; ++kc) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) mx = fmaxf(mx, sacc[nb][t]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;  // scale > 0: max commutes with it
-      // Lazy rescale: the reference max m_run only moves when a row's max
-      // exceeds it by more than 2^8 (so probabilities stay <= 256); the final
-      // O / l is the same for any reference, and the 64 multiplies of the O
-      // rescale are skipped for every tile that does not move it.
-      if (__any(mx > m_run + 8.f)) {
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - mn);
-        m_run = mn;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-      }
-      float psum = 0.f;
-      bf16x8 pB[4];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int db = 0; db < DB; ++db) {
+        bf16x4 part[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pr = fast_exp2(fmaf(sacc[nb][half * 8 + e], a.scale_log2, -m_run));
-            psum += pr;
-            pB[nb * 2 + half][e] = (__bf16)pr;
-          }
+          const int key = kc * 16 + tr_key + 4 * half;
+          const int el = db * 32 + tr_el;
+          const int pc = (el >> 3) ^ tile_swz<D>(key);
+          part[half] = lds_read_tr(sv + key * D + pc * 8 + (el & 7));
         }
-      }
-      l_run += psum;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint16_t* vp = &sV[buf][(kc * 16 + tr_key) * VS + db * 32 + tr_col];
-          const bf16x4 lo = lds_read_tr(vp);
-          const bf16x4 hi = lds_read_tr(vp + 4 * VS);
-          const bf16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pB[kc], oacc[db], 0, 0, 0);
-        }
+        const bf16x8 A = {part[0][0], part[0][1], part[0][2], part[0][3],
+                          part[1][0], part[1][1], part[1][2], part[1][3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pB[kc], oacc[db], 0, 0, 0);
       }
     }
-    // Stage the prefetched tile into the other buffer, then fetch the next.
-    if (kt + 1 < n_tiles) {
-      store_tile(buf ^ 1);
-      if (kt + 2 < n_tiles) load_tile(kt + 2);
-    }
-    __syncthreads();
+  };
+
+  int blk_next = 0;  // physical block of the next DMA request
+  if constexpr (DMA) {
+    if (NST - 1 < n_tiles) blk_next = bt[((NST - 1) * BN) >> bs_log2];
   }
 
-  if (!wave_active) return;
+  // One tile step on stage S = kt % NST: wait for this thread's requests of
+  // tile kt (later tiles' requests may stay in flight), publish them with the
+  // barrier -- which also tells every wave that stage (kt - 1) % NST, read
+  // during tile kt - 1, is free -- request tile kt + NST - 1 into it, compute.
+  auto step = [&](auto stage, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    uint16_t* sk = st[S];
+    uint16_t* nk = st[(S + NST - 1) % NST];
+    uint16_t* sv = sk + BN * D;
+    uint16_t* nv = nk + BN * D;
+    if constexpr (DMA) {
+      wait_tiles<2 * NI, NST - 2>(min(NST - 2, n_tiles - 1 - kt));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NST - 1 < n_tiles) {
+        request(nk, nv, kt + NST - 1, blk_next);
+        // The block of the next request is loaded a step ahead, so that the
+        // wave never waits on the block table.
+        if (kt + NST < n_tiles) blk_next = bt[((kt + NST) * BN) >> bs_log2];
+      }
+      if (wave_active && kt * BN <= kmax_wave) compute(sk, sv, kt);
+    } else {
+      __syncthreads();
+      if (kt + NST - 1 < n_tiles) fetch(kt + NST - 1);
+      if (wave_active && kt * BN <= kmax_wave) compute(sk, sv, kt);
+      if (kt + NST - 1 < n_tiles) deposit(nk, nv);
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) {
+    if (t < n_tiles) {
+      if constexpr (DMA) {
+        request(st[t], st[t] + BN * D, t, bt[(t * BN) >> bs_log2]);
+      } else {
+        fetch(t);
+        deposit(st[t], st[t] + BN * D);
+      }
+    }
+  }
+  {
+    const int qrow = row0 + lr;
+    if (wave_active && qrow < Lq) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((long)(q_start + qrow) * num_q_heads + h) * D + lh * 8;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) qB[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) qB[kk] = bf16x8{};
+    }
+  }
+  // The first tiles and Q are needed before any work: wait for everything
+  // here, so that no later wait for Q (which would also drain the tiles in
+  // flight) is needed inside the loop.
+  vm_wait<0>();
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  for (int kt = 0; kt < n_tiles; kt += NST) {
+    step(I0{}, kt);
+    if (kt + 1 >= n_tiles) break;
+    step(I1{}, kt + 1);
+    if constexpr (NST > 2) {
+      if (kt + 2 >= n_tiles) break;
+      step(I2{}, kt + 2);
+    }
+    if constexpr (NST > 3) {
+      if (kt + 3 >= n_tiles) break;
+      step(I3{}, kt + 3);
+    }
+  }
+
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_row < Lq) {
+  if (wave_active && my_row < Lq) {
     const float inv = 1.f / l_tot;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
-                   ((long)(q_start + my_row) * a.num_q_heads + h) * D;
+                   ((long)(q_start + my_row) * num_q_heads + h) * D;
     // Item t of block db is head-dim element db*32 + 8*(t/4) + 4*lh + t%4.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -308,23 +542,52 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   }
+  // Every wave is done with the LDS stages before the next item refills them.
+  __syncthreads();
+  }
+}
+
+template <int D, int HPW, bool DMA>
+static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t stream) {
+  constexpr int BN = PA_PREFILL_BN;
+  constexpr int NST = PA_PREFILL_NST;
+  // One workgroup per resident slot: CUs x the kernel's occupancy, queried
+  // once per device.
+  static int cached_device = -1, cached_slots = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev != cached_device) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(prefill_bf16_kernel<D, HPW, DMA, BN, NST>),
+            256, 0) != hipSuccess)
+      return -1;
+    cached_slots = max(1, cus * max(per_cu, 1));
+    cached_device = dev;
+  }
+  PrefillArgs p = a;
+  // (Tile counts are kept as 16-bit values: n_qt < 65536.)
+  p.persistent = (a.num_seqs <= kMaxPersistSeqs && a.max_seqlen_q < (1 << 21) &&
+                  n_items > cached_slots) ? 1 : 0;
+  const long long grid = p.persistent ? cached_slots : n_items;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST>), dim3((unsigned)grid), dim3(256),
+                     0, stream, p, a.block_tables, a.cu_seqlens_q, a.cu_seqlens_k);
+  return 0;
 }
 
 template <int D, int HPW>
 static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BMQ = 32 * (4 / HPW);
   const long long n_qt = (a.max_seqlen_q + BMQ - 1) / BMQ;
-  const long long grid =
+  const long long n_items =
       n_qt * a.num_seqs * (long long)a.num_kv_heads * (a.group / HPW);
-  if (grid <= 0) return 0;
-  if (grid > 0x7fffffffLL) return -1;
-  if (a.block_size_log2 >= 6)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, true>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, false>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, a);
-  return 0;
+  if (n_items <= 0) return 0;
+  if (n_items > 0x7fffffffLL) return -1;
+  if (a.block_size_log2 >= 0 && (1 << a.block_size_log2) >= PA_PREFILL_BN)
+    return launch_items<D, HPW, true>(a, n_items, stream);  // tiles inside one block
+  return launch_items<D, HPW, false>(a, n_items, stream);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {

@@ -37,7 +37,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("hq,hkv,d,dtype", SHAPES)
-@pytest.mark.parametrize("bs", [1, 16, 256])
+@pytest.mark.parametrize("bs", [1, 16, 32, 64, 256])
 def test_prefill_shapes_ragged(hq, hkv, d, dtype, bs):
     """Ragged tails, empty and one-token prompts, prefixes that do and do not
     end on a tile or block boundary."""
@@ -63,7 +63,7 @@ def test_prefill_invariance_bitwise():
     spec = PrefillSpec("pre-inv", 16, 8, 128, "bf16", 16, q_len_range=(1, 1),
                        q_lens=(40, 130, 1, 77), prefix_lens=(0, 20, 256, 5))
     ref = bits(run_prefill(make_prefill(spec, 83))[0])
-    for bs in (1, 4, 256):
+    for bs in (1, 4, 32, 64, 256):
         assert np.array_equal(bits(run_prefill(make_prefill(spec, 83, block_size=bs))[0]), ref)
     assert np.array_equal(bits(run_prefill(make_prefill(spec, 83, perm_seed=7))[0]), ref)
     case = make_prefill(spec, 83)
