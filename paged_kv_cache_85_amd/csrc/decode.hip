@@ -390,9 +390,18 @@ folded:
 
 // ---------------------------------------------------------------- persistent decode
 //
-// Items are ordered (sequence b, head chunk y, partition p), p fastest, so a
-// wave's consecutive items mostly share their query rows.  Wave w owns items
-// [w * n / W, (w + 1) * n / W).
+// Work is dealt in two parts, so that every wave gets a similar number of
+// stages to load while its consecutive items mostly share their query rows:
+//  * full partitions (P tokens), ordered (sequence b, head chunk y,
+//    partition p), p fastest: wave w takes an equal-count contiguous run;
+//  * the partial last partitions, ordered by size class (largest first, then
+//    (b, y)), dealt out in a snake that starts at the last wave -- the waves
+//    at the end of the grid are the ones with the shorter run of full
+//    partitions.
+// Which wave folds an item does not change the item's arithmetic.
+
+constexpr int kSizeClasses = 16;
+constexpr int kMaxDealSeqs = 4096;  // size classes kept in LDS up to this batch
 
 // Sum of x over the wave.
 __device__ __forceinline__ int wave_sum(int x) {
@@ -412,10 +421,22 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
 }
 
 struct ItemCursor {
-  int b, p, y;    // sequence, partition, head chunk
-  int L;          // context length of b
-  int t0, end;    // current stage start, end of the item's tokens
+  int b, p, y;     // sequence, partition, head chunk
+  int L;           // context length of b
+  int t0, end;     // current stage start, end of the item's tokens
+  int full_left;   // full partitions still to visit after the current item
+  int round;       // next round of the partial deal
 };
+
+// Wave-uniform description of the deal.  The per-sequence size classes and
+// the per-class item counts live in LDS, so that looking up the next item
+// never issues a vector load (it would wait behind the K/V stream).
+struct Deal {
+  int B, Y, P, W, w;
+  bool cls_in_lds;  // s_deal_cls holds the batch (else classes are recomputed)
+};
+__shared__ uint8_t s_deal_cls[kMaxDealSeqs];  // size class of each sequence
+__shared__ int s_deal_cnt[kSizeClasses];      // partial items per class, largest first
 
 // `lens` is the same array as a.context_lens, passed as a __restrict__
 // kernel argument: the kernel never writes it, so its reads can be scalar
@@ -425,24 +446,117 @@ __device__ __forceinline__ int seq_len(const RowAttnArgs& a, const int32_t* __re
   return b < a.num_rows ? min(lens[b], a.max_context) : 1;
 }
 
+__device__ __forceinline__ int full_parts(int L, int P) { return L > 0 ? L / P : 0; }
+
+// Size class of a sequence's partial last partition (0: none).
+__device__ __forceinline__ int tail_class(int L, int P) {
+  const int t = L > 0 ? L - (L / P) * P : 0;
+  return t > 0 ? (t * kSizeClasses + P - 1) / P : 0;
+}
+
 __device__ __forceinline__ void cursor_begin(ItemCursor& k, int P) {
   k.t0 = k.p * P;
   k.end = min(k.L, k.t0 + P);
 }
 
-__device__ __forceinline__ void cursor_next_item(ItemCursor& k, const RowAttnArgs& a,
-                                                 const int32_t* __restrict__ lens, int Y, int P) {
-  if (++k.p * P >= k.L) {
+// Full partition of rank `target` (in (b, y, p) order).
+__device__ __forceinline__ void seek_full(ItemCursor& k, long target, const Deal& d,
+                                          const RowAttnArgs& a,
+                                          const int32_t* __restrict__ lens, int lane) {
+  long acc = 0;
+  k.b = d.B;
+  int off = 0;
+  for (int base = 0; base < d.B; base += 64) {
+    const int b = base + lane;
+    const int ni = b < d.B ? d.Y * full_parts(min(lens[b], a.max_context), d.P) : 0;
+    const int incl = wave_scan(ni, lane);
+    const int chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    if (acc + chunk > target) {
+      const unsigned long long hit = __ballot(acc + incl > target);
+      const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+      const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
+      k.b = base + l0;
+      off = (int)(target - acc - excl);
+      break;
+    }
+    acc += chunk;
+  }
+  k.b = __builtin_amdgcn_readfirstlane(k.b);
+  k.L = seq_len(a, lens, k.b);
+  const int nf = max(full_parts(k.L, d.P), 1);
+  off = __builtin_amdgcn_readfirstlane(off);
+  k.y = off / nf;
+  k.p = off % nf;
+  cursor_begin(k, d.P);
+}
+
+__device__ __forceinline__ void next_full(ItemCursor& k, const Deal& d, const RowAttnArgs& a,
+                                          const int32_t* __restrict__ lens) {
+  if (++k.p >= full_parts(k.L, d.P)) {
     k.p = 0;
-    if (++k.y == Y) {
+    if (++k.y == d.Y) {
       k.y = 0;
       do {
         ++k.b;
         k.L = seq_len(a, lens, k.b);
-      } while (k.L <= 0);
+      } while (full_parts(k.L, d.P) == 0 && k.b < d.B);
     }
   }
-  cursor_begin(k, P);
+  cursor_begin(k, d.P);
+}
+
+// Rank of this wave's partial item in round r of the snake.
+__device__ __forceinline__ int partial_rank(const Deal& d, int r) {
+  return r * d.W + ((r & 1) ? d.w : d.W - 1 - d.w);
+}
+
+// Partial item of rank j (size class descending, then (b, y)).
+__device__ __forceinline__ void seek_partial(ItemCursor& k, int j, const Deal& d,
+                                             const RowAttnArgs& a,
+                                             const int32_t* __restrict__ lens, int lane) {
+  int c = 1;
+  for (int i = 0; i < kSizeClasses; ++i) {
+    const int n = __builtin_amdgcn_readfirstlane(s_deal_cnt[i]);
+    if (j < n) {
+      c = kSizeClasses - i;
+      break;
+    }
+    j -= n;
+  }
+  const int bi = j / d.Y;
+  k.y = j - bi * d.Y;
+  k.b = d.B;
+  int seen = 0;
+  for (int base = 0; base < d.B; base += 64) {
+    const int b = base + lane;
+    const bool in = b < d.B && (d.cls_in_lds ? (int)s_deal_cls[b]
+                                             : tail_class(min(lens[b], a.max_context), d.P)) == c;
+    const unsigned long long m = __ballot(in);
+    const int n = __popcll(m);
+    if (bi < seen + n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+      const unsigned long long sel = __ballot(in && below == bi - seen);
+      k.b = base + (int)__builtin_ctzll(sel);
+      break;
+    }
+    seen += n;
+  }
+  k.b = __builtin_amdgcn_readfirstlane(k.b);
+  k.L = seq_len(a, lens, k.b);
+  k.p = full_parts(k.L, d.P);  // the partial partition is the last one
+  cursor_begin(k, d.P);
+}
+
+__device__ __forceinline__ void cursor_next_item(ItemCursor& k, const Deal& d,
+                                                 const RowAttnArgs& a,
+                                                 const int32_t* __restrict__ lens, int lane) {
+  if (k.full_left > 0) {
+    --k.full_left;
+    next_full(k, d, a, lens);
+  } else {
+    seek_partial(k, partial_rank(d, k.round++), d, a, lens, lane);
+  }
 }
 
 template <typename E, int D, int HG>
@@ -456,59 +570,59 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
   const int lane = threadIdx.x;
   const int c = lane % LPR;
   const int r = lane / LPR;
-  const int B = a.num_rows;
-  const int P = a.part_tokens;
-  const int Y = a.num_kv_heads * a.head_chunks;
-  const int W = gridDim.x;
-  const int w = blockIdx.x;
+  Deal d;
+  d.B = a.num_rows;
+  d.P = a.part_tokens;
+  d.Y = a.num_kv_heads * a.head_chunks;
+  d.W = gridDim.x;
+  d.w = blockIdx.x;
+  const int B = d.B, P = d.P, Y = d.Y;
 
-  // Total partitions over the batch; wave 0 also zeroes rows whose length
-  // violates the precondition (no item covers them).
-  int total = 0;
+  // Full partitions and partial-partition classes over the batch; wave 0
+  // also zeroes rows whose length violates the precondition (no item covers
+  // them).
+  long n_full = 0;
+  d.cls_in_lds = B <= kMaxDealSeqs;
+  if (lane < kSizeClasses) s_deal_cnt[lane] = 0;
+  int n_partial = 0;
   for (int base = 0; base < B; base += 64) {
     const int b = base + lane;
     const int L = b < B ? min(lens[b], a.max_context) : 1;
-    if (w == 0 && L <= 0)
+    if (d.w == 0 && L <= 0)
       for (int i = 0; i < a.num_q_heads * D; ++i)
         E::store(reinterpret_cast<T*>(a.out) + (long)b * a.num_q_heads * D + i, 0.f);
-    total += __builtin_amdgcn_readfirstlane(wave_sum(b < B ? num_parts(L, P) : 0));
+    n_full += (long)Y * __builtin_amdgcn_readfirstlane(wave_sum(b < B ? full_parts(L, P) : 0));
+    const int cls = b < B ? tail_class(L, P) : 0;
+    if (d.cls_in_lds && b < B) s_deal_cls[b] = (uint8_t)cls;
+    // Lane i counts class kSizeClasses - i.
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kSizeClasses; ++i) {
+      const int n = Y * __popcll(__ballot(cls == kSizeClasses - i));
+      cnt = lane == i ? n : cnt;
+    }
+    if (lane < kSizeClasses) s_deal_cnt[lane] += cnt;
+    n_partial += __builtin_amdgcn_readfirstlane(wave_sum(lane < kSizeClasses ? cnt : 0));
   }
-  const long n_items = (long)total * Y;  // fits: total * Y <= rows * heads * parts
-  const long i0 = n_items * w / W;
-  const long i1 = n_items * (w + 1) / W;
-  int left = (int)(i1 - i0);
+  __syncthreads();
+
+  // This wave's run of full partitions, then its share of the partials.
+  const long fa = n_full / d.W, frem = n_full % d.W;
+  const long f0 = d.w < frem ? d.w * (fa + 1) : frem * (fa + 1) + (d.w - frem) * fa;
+  const int nfull_w = (int)(d.w < frem ? fa + 1 : fa);
+  const int rounds = n_partial / d.W, prem = n_partial % d.W;
+  const int npart_w = rounds + (((rounds & 1) ? d.w : d.W - 1 - d.w) < prem ? 1 : 0);
+  int left = nfull_w + npart_w;
   if (left <= 0) return;
 
-  // Locate the first item: sequence b holds Y * nparts(b) items.
   ItemCursor cp;
-  {
-    const long target = i0;
-    long acc = 0;
-    cp.b = B;
-    int off = 0;
-    for (int base = 0; base < B; base += 64) {
-      const int b = base + lane;
-      const int ni = b < B ? Y * num_parts(min(lens[b], a.max_context), P) : 0;
-      const int incl = wave_scan(ni, lane);
-      const int chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-      if (acc + chunk > target) {
-        const unsigned long long hit = __ballot(acc + incl > target);
-        const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
-        const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
-        cp.b = base + l0;
-        off = (int)(target - acc - excl);
-        break;
-      }
-      acc += chunk;
-    }
-    cp.b = __builtin_amdgcn_readfirstlane(cp.b);
-    if (cp.b >= B) return;  // unreachable when the wave owns items
-    cp.L = seq_len(a, lens, cp.b);
-    const int np = num_parts(cp.L, P);
-    off = __builtin_amdgcn_readfirstlane(off);
-    cp.y = off / np;
-    cp.p = off % np;
-    cursor_begin(cp, P);
+  cp.round = 0;
+  if (nfull_w > 0) {
+    cp.full_left = nfull_w - 1;
+    seek_full(cp, f0, d, a, lens, lane);
+  } else {
+    cp.full_left = 0;
+    seek_partial(cp, partial_rank(d, cp.round++), d, a, lens, lane);
   }
 
   const T* kc = reinterpret_cast<const T*>(a.k_cache);
@@ -556,7 +670,7 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
       ld.t0 += SUB;
     } else if (ld_left > 1) {
       --ld_left;
-      cursor_next_item(ld, a, lens, Y, P);
+      cursor_next_item(ld, d, a, lens, lane);
     }
   };
 
@@ -588,7 +702,7 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
         st.finish(a, (long)cp.b * a.num_q_heads + h0, num_parts(cp.L, P), cp.p, c, r);
         if (--left == 0) goto done;
         const int pb = cp.b, py = cp.y;
-        cursor_next_item(cp, a, lens, Y, P);
+        cursor_next_item(cp, d, a, lens, lane);
         if (cp.b != pb || cp.y != py) {  // new query rows (about once per wave)
           uint4 qraw[HG];
           load_q(qraw, cp);

@@ -114,7 +114,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 // tuned to the batch, so a row's arithmetic depends only on its own tokens:
 // the output is bitwise the same whether a sequence runs alone or batched,
 // whatever its physical block IDs or the block size.
-constexpr int kPartitionTokens = 256;
+#ifndef PA_DECODE_PARTITION
+#define PA_DECODE_PARTITION 256
+#endif
+constexpr int kPartitionTokens = PA_DECODE_PARTITION;
 
 static int heads_per_wg(int group, int head_dim) {
   const int cap = head_dim == 64 ? 8 : 4;
