@@ -102,14 +102,16 @@ def measured_traffic(name: str):
         return None
 
 
-def cpu_oracle_baseline(dec, pre4):
+def cpu_oracle_baseline(dec, pre4, threads=None):
     """The fp64 oracle, untuned, on this host: decode over the whole decode
-    workload and prefill over the varlen workload."""
+    workload and prefill over the varlen workload (input generation not
+    timed)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
 
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    if threads is None:
+        threads = max(1, min(os.cpu_count() or 1, 16))
     with threadpool_limits(limits=threads):
         used = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
         kc, vc = oracle.store_kv(dec.k_cache, dec.v_cache, dec.k_new, dec.v_new,
@@ -137,6 +139,7 @@ def cpu_oracle_baseline(dec, pre4):
 
 
 COPY_PROBE_BYTES = 1 << 30
+FLUSH_BYTES = 512 << 20
 
 
 def copy_probe(torch, dev) -> None:
@@ -152,12 +155,106 @@ def copy_probe(torch, dev) -> None:
     del src, dst
 
 
+def _median_us(torch, fn, stream, reps=20, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(stream)
+        fn()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    return t[reps // 2]
+
+
+def extras(torch, np, pa, dev, up, dec, stream):
+    """Rows beyond the step: the decode workload served as varlen rows
+    (Lq = 1), alone and mixed with prompts in one launch; and a small-batch
+    decode step replayed from a captured graph against eager calls."""
+    from synth import PrefillSpec, make_case, make_prefill
+    from paged_kv_cache_85_amd.graphs import DecodeGraph, bucket_size
+    res = {}
+    log("extras: decode rows and a mixed batch through pa_prefill_varlen")
+    L = dec.context_lens.astype(int)
+    prompts = (512, 512, 512, 512)
+    mixes = {"decode_as_varlen": ((1,) * len(L), tuple(int(x) - 1 for x in L)),
+             "mixed": ((1,) * len(L) + prompts, tuple(int(x) - 1 for x in L) + (0,) * 4)}
+    spec0 = PrefillSpec("mixed-qwen3", dec.num_q_heads, dec.num_kv_heads, dec.head_dim, "bf16",
+                        dec.block_size, q_len_range=(1, 1))
+    for name, (ql, pl) in mixes.items():
+        c = make_prefill(spec0, 95, q_lens=ql, prefix_lens=pl)
+        kc, vc = up(c.k_cache), up(c.v_cache)
+        pa.pa_store_kv(up(c.k_new), up(c.v_new), kc, vc, up(c.slot_mapping), stream=stream)
+        q = up(c.q)
+        out = torch.empty_like(q)
+        bt, cq, ck = up(c.block_tables), up(c.cu_seqlens_q), up(c.cu_seqlens_k)
+        us = _median_us(torch, lambda: pa.pa_prefill_varlen(
+            out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, float(c.scale),
+            stream=stream), stream)
+        res[name] = {"launch_us": round(us, 2), "sequences": c.num_seqs,
+                     "query_rows": c.total_q, "cached_tokens": int(c.k_lens.sum())}
+        del kc, vc, q, out
+    # the same prompts alone (the prefill half of the mixed launch)
+    c = make_prefill(spec0, 96, q_lens=prompts, prefix_lens=(0,) * 4)
+    kc, vc = up(c.k_cache), up(c.v_cache)
+    q = up(c.q)
+    out = torch.empty_like(q)
+    bt, cq, ck = up(c.block_tables), up(c.cu_seqlens_q), up(c.cu_seqlens_k)
+    res["prompts_alone_us"] = round(_median_us(torch, lambda: pa.pa_prefill_varlen(
+        out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, float(c.scale),
+        stream=stream), stream), 2)
+    del kc, vc, q, out
+    log("extras: graph-replayed decode steps (Qwen2.5-0.5B decode workload)")
+    c = make_case(2)
+    kc, vc = up(c.k_cache), up(c.v_cache)
+    q, kn, vn = up(c.q), up(c.k_new), up(c.v_new)
+    sl, cl, bt = up(c.slot_mapping), up(c.context_lens), up(c.block_tables)
+    out = torch.empty_like(q)
+    ws = torch.empty(pa.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim,
+                                                  c.max_context_len), dtype=torch.uint8,
+                     device=dev)
+
+    def eager():
+        pa.pa_store_kv(kn, vn, kc, vc, sl, stream=stream)
+        pa.pa_decode(out, q, kc, vc, bt, cl, c.max_context_len, float(c.scale), workspace=ws,
+                     stream=stream)
+
+    g = DecodeGraph(kc, vc, c.num_q_heads, bucket_size(c.num_seqs), bt.shape[1],
+                    c.max_context_len, float(c.scale))
+    g(q, kn, vn, sl, cl, bt)   # inputs now sit in the graph's static buffers
+    reps = 500
+
+    def wall(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e6
+
+    res["small_decode_step"] = {
+        "workload": f"store + decode, {c.num_seqs} sequences, Qwen2.5-0.5B heads, block 16",
+        "eager_us_per_step": round(wall(eager), 2),
+        "graph_us_per_step": round(wall(g.graph.replay), 2),
+        "gpu_us_eager": round(_median_us(torch, eager, stream), 2)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 512 MiB read that evicts L2 and the 256 MB MALL before "
+                         "each step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the mixed-batch and graph-replay measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a 1 GiB elementwise copy three times: "
                          "the known-size kernel that calibrates the HBM byte counters")
@@ -229,7 +326,20 @@ def main() -> int:
         pa.pa_prefill_varlen(s.out, s.q, s.kc, s.vc, s.bt, s.cq, s.ck, c.max_seqlen_q,
                              c.max_seqlen_k, float(c.scale), stream=stream)
 
-    stages = [("store_decode", lambda: store(D)), ("decode", lambda: decode(D)),
+    # Evict L2 and the MALL before each step by reading a 512 MiB buffer, so
+    # that no stage starts with its inputs cached by the previous step.  A read
+    # leaves clean lines behind (a write would leave dirty ones, whose
+    # write-back the next stage would pay).  Timed as a stage of its own and
+    # excluded from every rate.
+    flush_buf = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, dtype=torch.float32,
+                                                       device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.sum()
+
+    stages = [("flush", flush),
+              ("store_decode", lambda: store(D)), ("decode", lambda: decode(D)),
               ("store_prefill", lambda: store(P4)), ("prefill", lambda: prefill(P4)),
               ("store_prefix", lambda: store(P5)), ("prefix_prefill", lambda: prefill(P5))]
 
@@ -313,8 +423,14 @@ def main() -> int:
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(t5 / BF16_PEAK_TFLOPS, 4), "flops_per_launch": f5,
                              "avg_launch_us": round(avg["prefix_prefill"] * 1e6, 2)},
+            "median": {"varlen_tflops": round(f4 / med["prefill"] / 1e12, 2),
+                       "prefix_cache_tflops": round(f5 / med["prefix_prefill"] / 1e12, 2),
+                       "decode_gbs": round(dec_bytes / med["decode"] / 1e9, 2)},
         },
+        "cache_flush": None if args.no_flush else
+        f"{FLUSH_BYTES >> 20} MiB read before each step (own stage, excluded from rates)",
         "stages_us": {k: round(v * 1e6, 2) for k, v in avg.items()},
+        "stages_median_us": {k: round(v * 1e6, 2) for k, v in med.items()},
         "decode_path_gbs": round(dec_path_bytes / dec_path_s / 1e9, 2),
     }
     if not args.no_cpu_baseline:
@@ -322,6 +438,12 @@ def main() -> int:
         cpu = cpu_oracle_baseline(dec, pre4)
         result["cpu_baseline"] = cpu["decode"]
         result["cpu_baseline_prefill"] = cpu["prefill"]
+        log("timing the fp64 CPU oracle on one thread")
+        cpu1 = cpu_oracle_baseline(dec, pre4, threads=1)
+        result["cpu_baseline_1thread"] = {"decode": cpu1["decode"], "prefill": cpu1["prefill"]}
+    if not args.no_extras:
+        del D, P4, P5
+        result["next_rows"] = extras(torch, np, pa, dev, up, dec, stream)
     if args.copy_probe:
         copy_probe(torch, dev)
     print(json.dumps(result), flush=True)
