@@ -45,6 +45,7 @@ __all__ = [
 # paging (block size, block-ID permutation) never changes the logical content.
 _S_LENGTHS, _S_PREFIX_K, _S_PREFIX_V, _S_HIST_K, _S_HIST_V = 0, 1, 2, 3, 4
 _S_NEW_K, _S_NEW_V, _S_Q, _S_PAGING = 5, 6, 7, 8
+_S_PROLOGUE = 9
 
 _CHUNK = 1 << 22  # elements per independently seeded chunk of a normal draw
 
@@ -547,3 +548,63 @@ def logical_prefix(case: PrefillCase, b: int):
         return case.prefix_k, case.prefix_v
     lo, hi = case.prefix_off[b], case.prefix_off[b + 1]
     return case.prefix_k[lo:hi], case.prefix_v[lo:hi]
+
+
+# ---------------------------------------------------------------- store prologue
+
+@dataclass
+class PrologueCase:
+    """Raw projections of one step's new tokens plus what the store prologue
+    needs: per-head norm gains, token positions, the rotary table and the
+    pools (taken from an attention case, so the slots are real)."""
+    q: np.ndarray            # [T, Hq, D] storage dtype
+    k: np.ndarray            # [T, Hkv, D]
+    v: np.ndarray            # [T, Hkv, D]
+    q_weight: np.ndarray     # [D]
+    k_weight: np.ndarray     # [D]
+    positions: np.ndarray    # int32 [T]
+    cos_sin: np.ndarray      # float32 [max_position, D]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    slot_mapping: np.ndarray
+    dtype: str
+    eps: float
+
+
+def rope_table(max_position: int, head_dim: int, theta: float = 1.0e6) -> np.ndarray:
+    """The rotary table a model precomputes once (an input to both sides):
+    row p holds cos(p * f_i) for i < D/2, then sin(p * f_i), with
+    f_i = theta^(-2i/D); float64 arithmetic, stored as float32."""
+    half = head_dim // 2
+    f = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * f[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_prologue(config: int, seed: int, max_position: int = 4096,
+                  eps: float = 1e-6) -> PrologueCase:
+    """Projections for the new tokens of attention workload ``config``: the
+    same tokens, slots and pools, positions = each token's place in its
+    sequence."""
+    case = make_case(config)
+    dt = case.dtype
+    T, hkv, d = case.k_new.shape
+    hq = case.num_q_heads
+    rng = _rng(seed, _S_PROLOGUE)
+    def draw(shape, scale=1.0, mean=0.0):
+        x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale) + np.float32(mean))
+        return bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
+    q = draw((T, hq, d), 2.0)
+    k = draw((T, hkv, d), 2.0)
+    v = draw((T, hkv, d))
+    qw, kw = draw((d,), 0.1, 1.0), draw((d,), 0.1, 1.0)
+    if hasattr(case, "context_lens"):          # decode: the new token is the last one
+        pos = case.context_lens.astype(np.int64) - 1
+    else:                                      # prefill: the last Lq tokens of each sequence
+        pos = np.concatenate([np.arange(int(lk) - int(lq), int(lk)) for lq, lk in
+                              zip(case.q_lens, case.k_lens)]) if case.num_seqs else np.zeros(0)
+    pos = pos.astype(np.int32)
+    if pos.size and pos.max() >= max_position:
+        max_position = int(pos.max()) + 1
+    return PrologueCase(q, k, v, qw, kw, pos, rope_table(max_position, d), case.k_cache,
+                        case.v_cache, case.slot_mapping, dt, eps)

@@ -82,3 +82,39 @@ def test_mutation_is_caught(mid, find, repl, occ):
         except Exception:          # an assertion or a crash: the mistake is caught
             return
     pytest.fail(f"mutation {mid!r} passed every pin")
+
+
+# ---- the store-prologue oracle (QK RMS norm, rotary embedding, K/V store)
+import rope_pins
+
+PROLOGUE_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "store_prologue.py")
+PROLOGUE_MUTATIONS = [
+    ("rms-drops-eps", "np.sqrt(ms + eps)", "np.sqrt(ms)"),
+    ("rms-wrong-axis", "np.mean(x * x, axis=-1, keepdims=True)", "np.mean(x * x, axis=-2, keepdims=True)"),
+    ("rms-drops-gain", "/ np.sqrt(ms + eps) * w", "/ np.sqrt(ms + eps)"),
+    ("rope-sin-sign", "out[t, :, :half] = a * c - b * s", "out[t, :, :half] = a * c + b * s"),
+    ("rope-second-half-sign", "out[t, :, half:] = b * c + a * s", "out[t, :, half:] = b * c - a * s"),
+    ("rope-sin-cos-swapped", "c = cos_sin[positions[t], :half]", "c = cos_sin[positions[t], half:]"),
+    ("rope-position-off-by-one", "c = cos_sin[positions[t], :half]\n        s = cos_sin[positions[t], half:]",
+     "c = cos_sin[positions[t] + 1, :half]\n        s = cos_sin[positions[t] + 1, half:]"),
+    ("rope-interleaved-pairs", "a, b = y[t, :, :half], y[t, :, half:]", "a, b = y[t, :, 0::2], y[t, :, 1::2]"),
+    ("store-v-skips-slot-zero", "if s >= 0:", "if s > 0:"),
+    ("key-uses-query-gain", "rms_norm(kf, wk, eps)", "rms_norm(kf, wq, eps)"),
+]
+
+
+@pytest.mark.parametrize("mid,find,repl", PROLOGUE_MUTATIONS, ids=[m[0] for m in PROLOGUE_MUTATIONS])
+def test_prologue_mutation_is_caught(mid, find, repl):
+    with open(PROLOGUE_SRC) as f:
+        src = f.read()
+    assert src.count(find) == 1, find
+    src = src.replace(find, repl).replace("from .paged_attention import widen",
+                                          "from oracle.paged_attention import widen")
+    mod = types.ModuleType("prologue_mutant")
+    exec(compile(src, "<prologue mutant>", "exec"), mod.__dict__)
+    for check in rope_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:
+            return
+    pytest.fail(f"mutation {mid!r} passed every pin")
