@@ -206,6 +206,25 @@ def extras(torch, np, pa, dev, up, dec, stream):
         out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, float(c.scale),
         stream=stream), stream), 2)
     del kc, vc, q, out
+    log("extras: store prologue (QK norm + rotary + store) on the varlen prefill tokens")
+    from synth import make_prologue
+    pc = make_prologue(4, 31)
+    q, k, v = up(pc.q), up(pc.k), up(pc.v)
+    kc, vc = up(pc.k_cache), up(pc.v_cache)
+    qo = torch.empty_like(q)
+    qw, kw, cs = up(pc.q_weight), up(pc.k_weight), up(pc.cos_sin)
+    pos, sm = up(pc.positions), up(pc.slot_mapping)
+    T, hq, d = pc.q.shape
+    hkv = pc.k.shape[1]
+    us = _median_us(torch, lambda: pa.pa_qk_norm_rope_store(qo, q, k, v, qw, kw, cs, pos, kc, vc,
+                                                             sm, pc.eps, stream=stream), stream)
+    moved = 2 * T * (hq + 2 * hkv) * d * 2 + 8 * T   # read and write q, k, v rows; positions, slots
+    us_store = _median_us(torch, lambda: pa.pa_store_kv(k, v, kc, vc, sm, stream=stream), stream)
+    res["store_prologue"] = {"tokens": T, "launch_us": round(us, 2),
+                             "gbs": round(moved / us / 1e3, 1),
+                             "frac_of_hbm_peak": round(moved / us / 1e3 / HBM_PEAK_GBS, 4),
+                             "plain_store_us": round(us_store, 2)}
+    del q, k, v, kc, vc, qo
     log("extras: graph-replayed decode steps (Qwen2.5-0.5B decode workload)")
     c = make_case(2)
     kc, vc = up(c.k_cache), up(c.v_cache)

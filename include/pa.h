@@ -12,6 +12,8 @@
  *   pa_prefill_varlen  packed prompts (boundaries in cu_seqlens) attend
  *                      causally; with cu_seqlens_k > cu_seqlens_q the extra
  *                      keys are a cached prefix (prefix-cache hit).
+ *   pa_qk_norm_rope_store  the store with its prologue fused: per-head RMS
+ *                      norm and rotary embedding of queries and keys.
  *
  * Data model, shared by every call:
  *   K pool, V pool   [num_blocks, block_size, num_kv_heads, head_dim], row-major,
@@ -143,6 +145,40 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float scale,
                       int32_t dtype, void* stream);
+
+/*
+ * Store prologue: normalise and rotate the new tokens' queries and keys, then
+ * store keys and values -- the step between the projections and
+ * pa_store_kv's plain copy, in one pass.  For each token t and each head row
+ * x (D = head_dim elements) of q[t] and k[t]:
+ *     y_i = x_i / sqrt(mean_j(x_j^2) + eps) * w_i      (w = q_weight or k_weight)
+ *     for i < D/2, c = cos_sin[p][i], s = cos_sin[p][D/2 + i], p = positions[t]:
+ *         out_i = y_i * c - y_{i+D/2} * s,   out_{i+D/2} = y_{i+D/2} * c + y_i * s
+ * (the smzdm Nano-vLLM walk-through, model implementation details: Qwen3
+ * normalises queries and keys per head; "mini-vLLM", project summary: rotary
+ * embeddings).  Normalised, rotated queries go to q_out (which may be q
+ * itself); normalised, rotated keys and the raw values go to pool slot
+ * slot_mapping[t] as pa_store_kv does (negative slots are skipped).
+ * Arithmetic is fp32; results are rounded once to dtype (round to nearest
+ * even).
+ *   q, q_out      [num_tokens, num_q_heads, head_dim]
+ *   k, v          [num_tokens, num_kv_heads, head_dim]
+ *   q_weight, k_weight  [head_dim] gains, same dtype
+ *   cos_sin       float32 [max_position, head_dim]: cos in the first half of
+ *                 each row, sin in the second (the model's rotary table)
+ *   positions     int32 [num_tokens], each in [0, max_position) (clamped into
+ *                 range on the device; PA_CHECK=1 rejects violations)
+ *   head_dim      64 or 128; every element array and cos_sin 16-byte aligned
+ *   eps           finite, >= 0
+ * num_tokens == 0 is a no-op.
+ */
+int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void* v,
+                          const void* q_weight, const void* k_weight, const float* cos_sin,
+                          const int32_t* positions, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                          int32_t block_size, int32_t max_position, float eps, int32_t dtype,
+                          void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(int status);

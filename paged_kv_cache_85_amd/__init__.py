@@ -6,9 +6,10 @@ include/pa.h; this package only marshals torch device tensors into that ABI.
 """
 from .binding import (EXPORTS, LIB_PATH, PA_DTYPE_BF16, PA_DTYPE_F32, PA_E_HIP, PA_E_INVAL,
                       PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_OK, PAError, lib, pa_decode,
-                      pa_decode_workspace_bytes, pa_prefill_varlen, pa_status_string,
-                      pa_store_kv)
+                      pa_decode_workspace_bytes, pa_prefill_varlen, pa_qk_norm_rope_store,
+                      pa_status_string, pa_store_kv)
 
 __all__ = ["EXPORTS", "LIB_PATH", "PA_DTYPE_BF16", "PA_DTYPE_F32", "PA_E_HIP", "PA_E_INVAL",
            "PA_E_UNSUPPORTED", "PA_E_WORKSPACE", "PA_OK", "PAError", "lib", "pa_decode",
-           "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_status_string", "pa_store_kv"]
+           "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_qk_norm_rope_store",
+           "pa_status_string", "pa_store_kv"]

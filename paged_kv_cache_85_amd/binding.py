@@ -18,7 +18,7 @@ PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_varlen",
-           "pa_status_string")
+           "pa_qk_norm_rope_store", "pa_status_string")
 
 _lib = None
 
@@ -48,6 +48,9 @@ def lib() -> ctypes.CDLL:
         L.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, i32, i32, i32, f32, i32, vp]
         L.pa_prefill_varlen.restype = ctypes.c_int
+        L.pa_qk_norm_rope_store.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, i32, vp]
+        L.pa_qk_norm_rope_store.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -166,3 +169,27 @@ def pa_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_s
                                  int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, nb, bs,
                                  block_tables.shape[1], float(scale), dt, _stream(stream))
     _check("pa_prefill_varlen", rc)
+
+
+def pa_qk_norm_rope_store(q_out, q, k, v, q_weight, k_weight, cos_sin, positions, k_cache,
+                          v_cache, slot_mapping, eps: float, stream=None) -> None:
+    """q, q_out: [T, Hq, D]; k, v: [T, Hkv, D]; gains: [D]; cos_sin: float32
+    [max_position, D]; positions, slot_mapping: int32 [T]; pools [NB, BS, Hkv, D]."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or q_out.shape != q.shape or tuple(k.shape) != (T, hkv, d) or \
+            v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if q_weight.shape != (d,) or k_weight.shape != (d,) or cos_sin.dim() != 2 or \
+            cos_sin.shape[1] != d or positions.shape != (T,) or slot_mapping.shape != (T,):
+        raise ValueError("gains must be [D], cos_sin [P, D], positions/slot_mapping [T]")
+    rc = lib().pa_qk_norm_rope_store(
+        _ptr(q_out, "q_out", q.dtype), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(q_weight, "q_weight", q.dtype), _ptr(k_weight, "k_weight", q.dtype),
+        _ptr(cos_sin, "cos_sin", torch.float32), _ptr(positions, "positions", torch.int32),
+        _ptr(k_cache, "k_cache", q.dtype), _ptr(v_cache, "v_cache", q.dtype),
+        _ptr(slot_mapping, "slot_mapping", torch.int32), T, hq, hkv, d, nb, bs,
+        cos_sin.shape[0], float(eps), dt, _stream(stream))
+    _check("pa_qk_norm_rope_store", rc)

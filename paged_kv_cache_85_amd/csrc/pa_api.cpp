@@ -100,6 +100,66 @@ int pa_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
   return launch_status();
 }
 
+int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void* v,
+                          const void* q_weight, const void* k_weight, const float* cos_sin,
+                          const int32_t* positions, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                          int32_t block_size, int32_t max_position, float eps, int32_t dtype,
+                          void* stream) {
+  if (num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
+      block_size < 1 || max_position < 1 || !isfinite(eps) || eps < 0.f)
+    return PA_E_INVAL;
+  if (head_dim != 64 && head_dim != 128) return PA_E_UNSUPPORTED;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_E_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  const void* ptrs[] = {q_out, q, k, v, q_weight, k_weight, cos_sin, positions, k_cache,
+                        v_cache, slot_mapping};
+  for (const void* p : ptrs)
+    if (!p) return PA_E_INVAL;
+  // 16-byte rows of elements and of the cos/sin table are read whole.
+  for (const void* p : {(const void*)q_out, q, k, v, q_weight, k_weight, (const void*)cos_sin,
+                        (const void*)k_cache, (const void*)v_cache})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return PA_E_INVAL;
+  const long long num_slots = (long long)num_blocks * block_size;
+  if (num_slots > INT32_MAX) return PA_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (checks_enabled()) {
+    std::vector<int32_t> slots, pos;
+    if (!fetch(slots, slot_mapping, num_tokens, s)) return PA_E_HIP;
+    if (!fetch(pos, positions, num_tokens, s)) return PA_E_HIP;
+    std::vector<int32_t> seen;
+    for (int32_t x : slots) {
+      if (x >= num_slots) return PA_E_INVAL;
+      if (x >= 0) seen.push_back(x);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return PA_E_INVAL;
+    for (int32_t p : pos)
+      if (p < 0 || p >= max_position) return PA_E_INVAL;
+  }
+  pa::PrologueArgs a{};
+  a.q_out = q_out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_weight = q_weight;
+  a.k_weight = k_weight;
+  a.cos_sin = cos_sin;
+  a.positions = positions;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_position = max_position;
+  a.eps = eps;
+  a.num_slots = num_slots;
+  if (pa::launch_store_prologue(a, head_dim, dtype == PA_DTYPE_BF16, s)) return PA_E_INVAL;
+  return launch_status();
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;

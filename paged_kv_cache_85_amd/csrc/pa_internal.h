@@ -73,4 +73,27 @@ struct PrefillArgs {
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);
 
+struct PrologueArgs {
+  void* q_out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* q_weight;
+  const void* k_weight;
+  const float* cos_sin;
+  const int32_t* positions;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int num_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int max_position;
+  float eps;
+  long long num_slots;
+};
+
+int launch_store_prologue(const PrologueArgs& a, int head_dim, int dtype_bf16,
+                          hipStream_t stream);
+
 }  // namespace pa

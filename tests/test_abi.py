@@ -113,3 +113,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(ImportError):
         binding.lib()
+
+
+def _prologue(lib, **kw):
+    a = dict(qo=FAKE, q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, cs=FAKE, pos=FAKE, kc=FAKE,
+             vc=FAKE, sm=FAKE, T=4, hq=16, hkv=8, d=128, nb=64, bs=16, mp=4096, eps=1e-6,
+             dtype=1, stream=None)
+    a.update(kw)
+    return lib.pa_qk_norm_rope_store(a["qo"], a["q"], a["k"], a["v"], a["qw"], a["kw"], a["cs"],
+                                     a["pos"], a["kc"], a["vc"], a["sm"], a["T"], a["hq"],
+                                     a["hkv"], a["d"], a["nb"], a["bs"], a["mp"], a["eps"],
+                                     a["dtype"], a["stream"])
+
+
+def test_prologue_validation(lib):
+    assert _prologue(lib, d=96) == pa.PA_E_UNSUPPORTED
+    assert _prologue(lib, dtype=3) == pa.PA_E_UNSUPPORTED
+    assert _prologue(lib, eps=-1.0) == pa.PA_E_INVAL
+    assert _prologue(lib, eps=float("inf")) == pa.PA_E_INVAL
+    assert _prologue(lib, mp=0) == pa.PA_E_INVAL
+    assert _prologue(lib, kc=None) == pa.PA_E_INVAL
+    assert _prologue(lib, q=ctypes.c_void_p(0x1008)) == pa.PA_E_INVAL   # not 16-byte aligned
+    assert _prologue(lib, T=-1) == pa.PA_E_INVAL
+    assert _prologue(lib, T=0, q=None) == pa.PA_OK
