@@ -260,7 +260,60 @@ def extras(torch, np, pa, dev, up, dec, stream):
         "eager_us_per_step": round(wall(eager), 2),
         "graph_us_per_step": round(wall(g.graph.replay), 2),
         "gpu_us_eager": round(_median_us(torch, eager, stream), 2)}
+    res["block_manager"] = block_manager_rates(torch, np, pa, dec)
     return res
+
+
+def block_manager_rates(torch, np, pa, dec):
+    """Host cost of the block manager's per-step planning, into pinned host
+    buffers: a decode step of the decode workload (one batched append + the
+    tables and lengths), and a prefill step of the prefix-cache workload's
+    shape (64 prompts behind one shared 1024-token prefix: allocate with
+    prefix lookup, plan the packed rows, free)."""
+    log("extras: host block manager planning rates")
+    rng = np.random.default_rng(7)
+    bs = dec.block_size
+    L = dec.context_lens.astype(int)
+    B = len(L)
+    steps = 64
+    width = int((L.max() + steps) // bs + 2)
+    m = pa.BlockManager(int(sum(-(-(int(x) + steps) // bs) for x in L)) + 8, bs)
+    for i, n in enumerate(L):
+        m.allocate(i, rng.integers(0, 151936, int(n) - 1).astype(np.int32))
+    ids = np.arange(B, dtype=np.int64)
+    pin = {"block_tables": torch.zeros((B, width), dtype=torch.int32, pin_memory=True),
+           "context_lens": torch.zeros(B, dtype=torch.int32, pin_memory=True)}
+    toks = rng.integers(0, 151936, (steps, B)).astype(np.int32)
+    t_dec = []
+    for s in range(steps):
+        t = time.perf_counter()
+        _, n_ok = m.append_batch(ids, toks[s])
+        m.plan_decode(ids, width, out=pin)
+        t_dec.append(time.perf_counter() - t)
+        assert n_ok == B
+    prefix = rng.integers(0, 151936, 1024).astype(np.int32)
+    pm = pa.BlockManager(64 * 6 + 8, bs)
+    prompts = [np.concatenate([prefix, rng.integers(0, 151936, int(k)).astype(np.int32)])
+               for k in rng.integers(64, 513, 64)]
+    pid = np.arange(64, dtype=np.int64)
+    rows = sum(len(p) for p in prompts)
+    ppin = {"block_tables": torch.zeros((64, 8), dtype=torch.int32, pin_memory=True),
+            "cu_seqlens_q": torch.zeros(65, dtype=torch.int32, pin_memory=True),
+            "cu_seqlens_k": torch.zeros(65, dtype=torch.int32, pin_memory=True),
+            "slot_mapping": torch.zeros(rows, dtype=torch.int32, pin_memory=True)}
+    t_pre, cached = [], 0
+    for r in range(21):
+        t = time.perf_counter()
+        cached = sum(pm.allocate(i, p) for i, p in enumerate(prompts))
+        pm.plan_prefill(pid, 8, out=ppin)
+        for i in range(64):
+            pm.free(i)
+        if r:                                      # the first pass fills the cache
+            t_pre.append(time.perf_counter() - t)
+    return {"decode_step": {"sequences": B, "block_size": bs,
+                            "us_per_step": round(float(np.median(t_dec)) * 1e6, 1)},
+            "prefill_step": {"sequences": 64, "prompt_tokens": rows, "cached_tokens": cached,
+                             "us_per_step": round(float(np.median(t_pre)) * 1e6, 1)}}
 
 
 def main() -> int:

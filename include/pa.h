@@ -64,7 +64,8 @@ enum {
   PA_E_INVAL = -1,        /* null pointer, bad size, Hq % Hkv != 0, bad index data */
   PA_E_UNSUPPORTED = -2,  /* head_dim or dtype outside what the kernels cover */
   PA_E_WORKSPACE = -3,    /* decode workspace too small */
-  PA_E_HIP = -4           /* HIP runtime error while launching */
+  PA_E_HIP = -4,          /* HIP runtime error while launching */
+  PA_E_NOMEM = -5         /* block manager: not enough free blocks (nothing changed) */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
@@ -179,6 +180,84 @@ int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void*
                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                           int32_t block_size, int32_t max_position, float eps, int32_t dtype,
                           void* stream);
+
+/*
+ * Host block manager: the CPU bookkeeping that produces the kernels' paging
+ * inputs ("nano-vLLM Part 4", section 1: block IDs, reference counts and
+ * prefix-hash metadata live on the CPU; "mini-vLLM", features list: a fixed
+ * pool of blocks with an O(1) free-list allocator and a block table per
+ * sequence).  Full blocks are registered under their token content chained
+ * with their predecessor, so a sequence starting with the same full blocks
+ * shares them (reference counts) -- an exact full-block prefix cache (smzdm
+ * Nano-vLLM walk-through, scheduling and memory).  A freed block keeps its
+ * registration until the free list (first in, first out) hands it out again,
+ * so a preempted sequence that is allocated again finds its computed blocks.
+ * Sequences are named by caller-chosen 64-bit IDs.  The object is not
+ * thread-safe; it never touches the GPU.  Block IDs are indices into the
+ * pools given to the kernels (num_blocks must match).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager over num_blocks blocks of block_size tokens; NULL on bad sizes. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* m);
+/* Blocks on the free list (cached blocks with no user count as free). */
+int32_t pa_bm_num_free(const pa_block_manager* m);
+/* Blocks for a new sequence's prompt tokens[0 .. num_tokens): reuses cached
+ * full blocks from the start while they match, then takes fresh ones.
+ * *num_cached_tokens = the leading tokens whose K/V the pool already holds
+ * (at most num_tokens - 1: the last token is always recomputed).  Returns
+ * PA_E_NOMEM (and changes nothing) when the pool is short, PA_E_INVAL for a
+ * known seq_id or an empty prompt. */
+int pa_bm_allocate(pa_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                   int32_t num_tokens, int32_t* num_cached_tokens);
+/* Append one decoded token; *slot = its pool slot (block * block_size +
+ * offset), taking a new block when the token opens one (PA_E_NOMEM if none
+ * is free) and registering the block when the token fills it. */
+int pa_bm_append(pa_block_manager* m, int64_t seq_id, int32_t token, int32_t* slot);
+/* Release a sequence (finished or preempted): each block's count drops, and
+ * blocks reaching zero go to the free list, last block first. */
+int pa_bm_free(pa_block_manager* m, int64_t seq_id);
+/* The sequence's block table; *num_blocks gets its length (PA_E_INVAL if it
+ * exceeds capacity; out may be NULL to ask for the length). */
+int pa_bm_block_table(const pa_block_manager* m, int64_t seq_id, int32_t* out,
+                      int32_t capacity, int32_t* num_blocks);
+/* Token count and cached-prefix length of a sequence. */
+int pa_bm_seq_info(const pa_block_manager* m, int64_t seq_id, int32_t* num_tokens,
+                   int32_t* num_cached_tokens);
+/* Slots of tokens [first, first + count) of a sequence (the slot mapping of
+ * a step's new tokens). */
+int pa_bm_slots(const pa_block_manager* m, int64_t seq_id, int32_t first, int32_t count,
+                int32_t* slots);
+
+/* Batched forms for a scheduler's step (one call per step instead of one
+ * per sequence).  All buffers are host memory owned by the caller; block
+ * table rows are padded with block 0 past each sequence's blocks.
+ *
+ * Append tokens[i] to seq_ids[i] for i in order.  Stops at the first
+ * sequence whose new token needs a block when none is free: returns
+ * PA_E_NOMEM with *num_done = the appends made (kept; slots[0 .. num_done)
+ * valid), so the caller can preempt and continue from there.  PA_E_INVAL
+ * for an unknown ID, with *num_done likewise. */
+int pa_bm_append_batch(pa_block_manager* m, const int64_t* seq_ids, const int32_t* tokens,
+                       int32_t num_seqs, int32_t* slots, int32_t* num_done);
+/* Decode-step inputs: block_tables [num_seqs, table_width], context_lens
+ * [num_seqs] (token counts), *max_context_len.  PA_E_INVAL (nothing
+ * written) for an unknown ID or a table wider than table_width. */
+int pa_bm_plan_decode(const pa_block_manager* m, const int64_t* seq_ids, int32_t num_seqs,
+                      int32_t table_width, int32_t* block_tables, int32_t* context_lens,
+                      int32_t* max_context_len);
+/* Prefill-step inputs for sequences just allocated: the query rows of
+ * sequence i are its tokens past the cached prefix.  block_tables
+ * [num_seqs, table_width]; cu_seqlens_q / cu_seqlens_k [num_seqs + 1];
+ * slot_mapping [sum of query rows] (the store's slots, in packed row order);
+ * *max_seqlen_q / *max_seqlen_k.  PA_E_INVAL (nothing written) for an
+ * unknown ID, a table wider than table_width or more query rows than
+ * slot_capacity. */
+int pa_bm_plan_prefill(const pa_block_manager* m, const int64_t* seq_ids, int32_t num_seqs,
+                       int32_t table_width, int32_t* block_tables, int32_t* cu_seqlens_q,
+                       int32_t* cu_seqlens_k, int32_t* slot_mapping, int32_t slot_capacity,
+                       int32_t* max_seqlen_q, int32_t* max_seqlen_k);
 
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(int status);

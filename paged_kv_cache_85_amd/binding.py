@@ -12,13 +12,16 @@ import ctypes
 import os
 from typing import Optional
 
-PA_OK, PA_E_INVAL, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP = 0, -1, -2, -3, -4
+PA_OK, PA_E_INVAL, PA_E_UNSUPPORTED, PA_E_WORKSPACE, PA_E_HIP, PA_E_NOMEM = 0, -1, -2, -3, -4, -5
 PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_varlen",
-           "pa_qk_norm_rope_store", "pa_status_string")
+           "pa_qk_norm_rope_store", "pa_status_string", "pa_bm_create", "pa_bm_destroy",
+           "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append", "pa_bm_free", "pa_bm_block_table",
+           "pa_bm_seq_info", "pa_bm_slots", "pa_bm_append_batch", "pa_bm_plan_decode",
+           "pa_bm_plan_prefill")
 
 _lib = None
 
@@ -51,6 +54,28 @@ def lib() -> ctypes.CDLL:
         L.pa_qk_norm_rope_store.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                             i32, i32, i32, i32, i32, f32, i32, vp]
         L.pa_qk_norm_rope_store.restype = ctypes.c_int
+        i64, pi32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+        L.pa_bm_create.argtypes = [i32, i32]
+        L.pa_bm_create.restype = vp
+        L.pa_bm_destroy.argtypes = [vp]
+        L.pa_bm_destroy.restype = None
+        L.pa_bm_num_free.argtypes = [vp]
+        L.pa_bm_num_free.restype = i32
+        L.pa_bm_allocate.argtypes = [vp, i64, vp, i32, pi32]
+        L.pa_bm_append.argtypes = [vp, i64, i32, pi32]
+        L.pa_bm_free.argtypes = [vp, i64]
+        L.pa_bm_block_table.argtypes = [vp, i64, pi32, i32, pi32]
+        L.pa_bm_seq_info.argtypes = [vp, i64, pi32, pi32]
+        L.pa_bm_slots.argtypes = [vp, i64, i32, i32, pi32]
+        # array arguments travel as plain addresses (c_void_p): far cheaper
+        # per call than typed ctypes pointers
+        L.pa_bm_append_batch.argtypes = [vp, vp, vp, i32, vp, pi32]
+        L.pa_bm_plan_decode.argtypes = [vp, vp, i32, i32, vp, vp, pi32]
+        L.pa_bm_plan_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, pi32, pi32]
+        for f in ("pa_bm_allocate", "pa_bm_append", "pa_bm_free", "pa_bm_block_table",
+                  "pa_bm_seq_info", "pa_bm_slots", "pa_bm_append_batch", "pa_bm_plan_decode",
+                  "pa_bm_plan_prefill"):
+            getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -193,3 +218,164 @@ def pa_qk_norm_rope_store(q_out, q, k, v, q_weight, k_weight, cos_sin, positions
         _ptr(slot_mapping, "slot_mapping", torch.int32), T, hq, hkv, d, nb, bs,
         cos_sin.shape[0], float(eps), dt, _stream(stream))
     _check("pa_qk_norm_rope_store", rc)
+
+
+class BlockManager:
+    """Host block manager of libpa (pa_bm_* in include/pa.h): block tables,
+    slot mapping and prefix-cache hits for sequences of token IDs.  Runs on
+    the CPU; its block IDs index the pools given to the kernels."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = lib()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("bad block manager sizes")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_bm_destroy(h)
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def allocate(self, seq_id: int, tokens) -> int:
+        """Blocks for a new sequence's prompt; returns its cached-prefix length."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check("pa_bm_allocate", self._lib.pa_bm_allocate(self._h, int(seq_id), t.ctypes.data,
+                                                           t.size, ctypes.byref(cached)))
+        return int(cached.value)
+
+    def append(self, seq_id: int, token: int) -> int:
+        """One decoded token; returns its pool slot."""
+        slot = ctypes.c_int32(0)
+        _check("pa_bm_append", self._lib.pa_bm_append(self._h, int(seq_id), int(token),
+                                                       ctypes.byref(slot)))
+        return int(slot.value)
+
+    def free(self, seq_id: int) -> None:
+        _check("pa_bm_free", self._lib.pa_bm_free(self._h, int(seq_id)))
+
+    def seq_info(self, seq_id: int):
+        n, c = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check("pa_bm_seq_info", self._lib.pa_bm_seq_info(self._h, int(seq_id), ctypes.byref(n),
+                                                           ctypes.byref(c)))
+        return int(n.value), int(c.value)
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        n = ctypes.c_int32(0)
+        # the first call only asks for the length (it reports a short buffer)
+        self._lib.pa_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n))
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check("pa_bm_block_table", self._lib.pa_bm_block_table(
+            self._h, int(seq_id), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size,
+            ctypes.byref(n)))
+        return out[:n.value]
+
+    def slots(self, seq_id: int, first: int, count: int):
+        import numpy as np
+        out = np.zeros(max(count, 1), np.int32)
+        _check("pa_bm_slots", self._lib.pa_bm_slots(
+            self._h, int(seq_id), int(first), int(count),
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return out[:count]
+
+    def append_batch(self, seq_ids, tokens):
+        """Append tokens[i] to seq_ids[i] in order.  Returns (slots, done):
+        on a shortage it stops, keeping the first `done` appends."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        if ids.shape != tok.shape:
+            raise ValueError("one token per sequence")
+        slots = np.zeros(max(ids.size, 1), np.int32)
+        done = ctypes.c_int32(0)
+        rc = self._lib.pa_bm_append_batch(self._h, _i64p(ids), _i32p(tok), ids.size, _i32p(slots),
+                                          ctypes.byref(done))
+        if rc not in (PA_OK, PA_E_NOMEM):
+            raise PAError("pa_bm_append_batch", rc)
+        return slots[:done.value], int(done.value)
+
+    def _width(self, ids):
+        """Widest block table among the sequences (at least 1)."""
+        w = 1
+        for sid in ids:
+            n = ctypes.c_int32(0)
+            self._lib.pa_bm_block_table(self._h, int(sid), None, 0, ctypes.byref(n))
+            w = max(w, n.value)
+        return w
+
+    def plan_prefill(self, seq_ids, table_width: int, out=None):
+        """Prefill-step inputs of sequences just allocated (the rows past each
+        cached prefix), filled by one native call.  `out` may hold
+        preallocated (pinned) int32 host tensors or arrays named block_tables
+        [B, table_width], cu_seqlens_q / cu_seqlens_k [B + 1] and slot_mapping
+        (capacity); returns dict with those (slot_mapping trimmed to the rows)
+        and the max lengths."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B = ids.size
+        if out is None:
+            rows = sum(self.seq_info(s)[0] - self.seq_info(s)[1] for s in ids)
+            out = {"block_tables": np.zeros((B, table_width), np.int32),
+                   "cu_seqlens_q": np.zeros(B + 1, np.int32),
+                   "cu_seqlens_k": np.zeros(B + 1, np.int32),
+                   "slot_mapping": np.zeros(max(rows, 1), np.int32)}
+        mq, mk = ctypes.c_int32(0), ctypes.c_int32(0)
+        sm = out["slot_mapping"]
+        _check("pa_bm_plan_prefill", self._lib.pa_bm_plan_prefill(
+            self._h, _i64p(ids), B, int(table_width), _i32p(out["block_tables"]),
+            _i32p(out["cu_seqlens_q"]), _i32p(out["cu_seqlens_k"]), _i32p(sm), _numel(sm),
+            ctypes.byref(mq), ctypes.byref(mk)))
+        res = dict(out)
+        res["slot_mapping"] = sm[:int(out["cu_seqlens_q"][B])]
+        res["max_seqlen_q"], res["max_seqlen_k"] = int(mq.value), int(mk.value)
+        return res
+
+    def plan_decode(self, seq_ids, table_width: int, out=None):
+        """Decode-step inputs (block_tables [B, table_width], context_lens [B])
+        by one native call; `out` as in plan_prefill."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B = ids.size
+        if out is None:
+            out = {"block_tables": np.zeros((B, table_width), np.int32),
+                   "context_lens": np.zeros(B, np.int32)}
+        mx = ctypes.c_int32(0)
+        _check("pa_bm_plan_decode", self._lib.pa_bm_plan_decode(
+            self._h, _i64p(ids), B, int(table_width), _i32p(out["block_tables"]),
+            _i32p(out["context_lens"]), ctypes.byref(mx)))
+        res = dict(out)
+        res["max_context_len"] = int(mx.value)
+        return res
+
+    def prefill_inputs(self, seq_ids, table_width: int = 0):
+        """plan_prefill with numpy outputs, tables as wide as needed."""
+        return self.plan_prefill(seq_ids, max(table_width, self._width(seq_ids)))
+
+    def decode_inputs(self, seq_ids, table_width: int = 0):
+        """plan_decode with numpy outputs, tables as wide as needed."""
+        return self.plan_decode(seq_ids, max(table_width, self._width(seq_ids)))
+
+
+def _i32p(a):
+    """Address of a contiguous int32 numpy array or host torch tensor."""
+    if hasattr(a, "data_ptr"):
+        assert str(a.dtype) == "torch.int32" and a.is_contiguous() and not a.is_cuda
+        return a.data_ptr()
+    assert a.dtype == "int32" and a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _i64p(a):
+    assert a.dtype == "int64" and a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _numel(a):
+    return int(a.numel()) if hasattr(a, "numel") else int(a.size)

@@ -66,6 +66,7 @@ const char* pa_status_string(int status) {
     case PA_E_UNSUPPORTED: return "unsupported head_dim, dtype or shape";
     case PA_E_WORKSPACE: return "decode workspace too small";
     case PA_E_HIP: return "HIP runtime error";
+    case PA_E_NOMEM: return "not enough free blocks";
     default: return "unknown status";
   }
 }

@@ -38,7 +38,7 @@ __all__ = [
     "DecodeSpec", "PrefillSpec", "DecodeCase", "PrefillCase", "CONFIGS",
     "make_decode", "make_prefill", "make_case", "bf16_bits", "poison_bits",
     "decode_subset", "prefill_subset", "logical_prefix",
-    "storage_np_dtype",
+    "storage_np_dtype", "token_rows",
 ]
 
 # Named random streams; each is its own SeedSequence so that changing the
@@ -46,6 +46,7 @@ __all__ = [
 _S_LENGTHS, _S_PREFIX_K, _S_PREFIX_V, _S_HIST_K, _S_HIST_V = 0, 1, 2, 3, 4
 _S_NEW_K, _S_NEW_V, _S_Q, _S_PAGING = 5, 6, 7, 8
 _S_PROLOGUE = 9
+_S_TOKEN_ROWS = 10
 
 _CHUNK = 1 << 22  # elements per independently seeded chunk of a normal draw
 
@@ -608,3 +609,23 @@ def make_prologue(config: int, seed: int, max_position: int = 4096,
         max_position = int(pos.max()) + 1
     return PrologueCase(q, k, v, qw, kw, pos, rope_table(max_position, d), case.k_cache,
                         case.v_cache, case.slot_mapping, dt, eps)
+
+
+# --------------------------------------------------------------------------- token rows
+
+def token_rows(tokens: Sequence[int], positions: Sequence[int], row_shape: Tuple[int, ...],
+               dtype: str, seed: int, which: int) -> np.ndarray:
+    """Rows that stand in for a model's per-token projections: row i is a
+    N(0, 1) draw determined by (seed, which, tokens[i], positions[i]) alone,
+    so a token at a given position always yields the same row, whichever
+    sequence, batch or step it is computed in.  `which` picks independent
+    families (say 0 = query, 1 = key, 2 = value).  Returns
+    [len(tokens)] + row_shape in the storage type."""
+    n = len(tokens)
+    out = np.empty((n,) + tuple(row_shape), storage_np_dtype(dtype))
+    m = int(np.prod(row_shape))
+    for i, (t, p) in enumerate(zip(tokens, positions)):
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(_S_TOKEN_ROWS, which, int(t), int(p)))
+        x = np.random.Generator(np.random.PCG64(ss)).standard_normal(m, dtype=np.float32)
+        out[i] = (bf16_bits(x) if dtype == "bf16" else x).reshape(row_shape)
+    return out

@@ -118,3 +118,41 @@ def test_prologue_mutation_is_caught(mid, find, repl):
         except Exception:
             return
     pytest.fail(f"mutation {mid!r} passed every pin")
+
+
+# ---- the block-manager model (free list, prefix cache, slots)
+import test_block_manager
+
+BM_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "block_manager.py")
+BM_MUTATIONS = [
+    ("full-hit-not-recomputed", "cached = min(cached, n - 1)", "cached = cached"),
+    ("free-list-lifo", "self.free.popitem(last=False)", "self.free.popitem(last=True)"),
+    ("reused-block-keeps-key", "del self.registry[self.key[b]]", "pass"),
+    ("release-front-to-back", 'for b in reversed(s["blocks"]):', 'for b in s["blocks"]:'),
+    ("slot-offset", "return b * bs + n % bs", "return b * bs + (n + 1) % bs"),
+    ("append-never-registers", 'self._register(b, tuple(s["tokens"][:n + 1]))', "pass"),
+    ("partial-block-cached", ("for i in range(n // bs):", "if (i + 1) * bs <= n:"),
+     ("for i in range(nblocks):", "if True:")),
+    ("hit-stays-on-free-list", "del self.free[b]\n", "pass\n"),
+    ("release-ignores-refcount", "if self.ref[b] == 0:", "if True:"),
+]
+
+
+@pytest.mark.parametrize("mid,find,repl", BM_MUTATIONS, ids=[m[0] for m in BM_MUTATIONS])
+def test_block_model_mutation_is_caught(mid, find, repl):
+    with open(BM_SRC) as f:
+        src = f.read()
+    finds, repls = (find, repl) if isinstance(find, tuple) else ((find,), (repl,))
+    for f_, r_ in zip(finds, repls):
+        assert src.count(f_) == 1, f_
+        src = src.replace(f_, r_)
+    # the mutant raises the real shortage error, so the checks recognise it
+    src = src.replace("class NoMemory(Exception):\n    pass", "from oracle.block_manager import NoMemory")
+    mod = types.ModuleType("block_mutant")
+    exec(compile(src, "<block-manager mutant>", "exec"), mod.__dict__)
+    for check in test_block_manager.MODEL_PINS + [test_block_manager.model_invariants]:
+        try:
+            check(mod.BlockModel)
+        except (Exception, pytest.fail.Exception):  # a missing pytest.raises error is a catch
+            return
+    pytest.fail(f"mutation {mid!r} passed every pin")
