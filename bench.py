@@ -231,7 +231,7 @@ def extras(torch, np, pa, dev, up, dec, stream):
     q, kn, vn = up(c.q), up(c.k_new), up(c.v_new)
     sl, cl, bt = up(c.slot_mapping), up(c.context_lens), up(c.block_tables)
     out = torch.empty_like(q)
-    ws = torch.empty(pa.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim,
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim,
                                                   c.max_context_len), dtype=torch.uint8,
                      device=dev)
 
@@ -374,7 +374,7 @@ def main() -> int:
             s.cl = up(case.context_lens)
             n = pa.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
                                              case.max_context_len)
-            s.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+            s.ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
         else:
             s.cq, s.ck = up(case.cu_seqlens_q), up(case.cu_seqlens_k)
         return s

@@ -91,9 +91,10 @@ int pa_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
                 void* stream);
 
 /*
- * Bytes of fp32 workspace pa_decode may need for split-context partial
- * results (running max, sum and unnormalised output per sequence, query head
- * and context partition).  Depends only on these sizes.
+ * Bytes of workspace pa_decode may need: a 256-byte work counter, then fp32
+ * split-context partial results (running max, sum and unnormalised output
+ * per sequence, query head and context partition).  Depends only on these
+ * sizes.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len);
@@ -111,8 +112,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   max_context_len  host upper bound of context_lens (sizes the grid)
  *   workspace     device memory of at least
  *                 pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
- *                 max_context_len) bytes, 256-byte aligned; its contents on
- *                 entry do not matter and are overwritten.
+ *                 max_context_len) bytes, 256-byte aligned.  Its first 256
+ *                 bytes hold a work counter that must be zero before the
+ *                 first call that uses this memory as a workspace (clear it
+ *                 once, e.g. with hipMemset); every call leaves it zero
+ *                 again, so a workspace can be reused by any later call on
+ *                 the same stream.  The rest is scratch.  Calls that run
+ *                 concurrently need workspaces of their own.
  * num_seqs == 0 is a no-op.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -150,7 +150,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
               scale: float, workspace=None, stream=None) -> None:
     """q, out: [B, Hq, D]; block_tables: int32 [B, MB]; context_lens: int32 [B].
     workspace: a device tensor of at least pa_decode_workspace_bytes(...) bytes
-    (allocated here through torch when None)."""
+    whose first 256 bytes were zeroed before its first use (every call leaves
+    them zero); allocated and zeroed here through torch when None."""
     torch = _torch()
     dt = _dtype_code(q)
     B, hq, d = q.shape
@@ -161,7 +162,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
         raise ValueError("block_tables must be [B, MB] and context_lens [B]")
     if workspace is None:
         n = pa_decode_workspace_bytes(B, hq, d, max_context_len)
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().pa_decode(_ptr(out, "out", q.dtype), _ptr(q, "q"),
                          _ptr(k_cache, "k_cache", q.dtype), _ptr(v_cache, "v_cache", q.dtype),

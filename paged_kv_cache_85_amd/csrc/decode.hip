@@ -390,18 +390,32 @@ folded:
 
 // ---------------------------------------------------------------- persistent decode
 //
-// Work is dealt in two parts, so that every wave gets a similar number of
-// stages to load while its consecutive items mostly share their query rows:
-//  * full partitions (P tokens), ordered (sequence b, head chunk y,
-//    partition p), p fastest: wave w takes an equal-count contiguous run;
-//  * the partial last partitions, ordered by size class (largest first, then
-//    (b, y)), dealt out in a snake that starts at the last wave -- the waves
-//    at the end of the grid are the ones with the shorter run of full
-//    partitions.
-// Which wave folds an item does not change the item's arithmetic.
+// Items are numbered by a code: [0, n_full) are the full partitions (P
+// tokens) in (sequence b, head chunk y, partition p) order, p fastest;
+// [n_full, n_full + n_partial) are the partial last partitions, largest size
+// class first, then (b, y).
+//
+// Every wave first folds an equal-count contiguous run of full partitions
+// (consecutive items mostly share their query rows).  Waves on a loaded chip
+// do not stream at equal rates (the XCDs and the slots within a CU differ),
+// so a static deal of everything leaves the last waves running alone.  With a
+// ticket counter (the decode workspace holds one), the static runs cover only
+// part of the full partitions; the rest, then the partials, largest first,
+// are handed out one ticket at a time to whichever wave is free.  Each wave
+// draws until a draw comes back past the last item, so a launch of W waves
+// makes exactly W such draws; the wave that draws the very last value knows
+// that no one will touch the counter again and puts it back to zero, so
+// every call leaves the counter as it found it (zero).  Without a
+// counter (one-partition batches: no workspace) the partials are dealt in a
+// snake over size classes that starts at the waves with the shorter static
+// run.  Which wave folds an item does not change the item's arithmetic.
 
 constexpr int kSizeClasses = 16;
-constexpr int kMaxDealSeqs = 4096;  // size classes kept in LDS up to this batch
+constexpr int kMaxDealSeqs = 4096;  // per-sequence deal tables kept in LDS up to this batch
+#ifndef PA_DECODE_STATIC_PCT
+#define PA_DECODE_STATIC_PCT 60
+#endif
+constexpr int kStaticPct = PA_DECODE_STATIC_PCT;  // full partitions dealt statically (percent)
 
 // Sum of x over the wave.
 __device__ __forceinline__ int wave_sum(int x) {
@@ -424,19 +438,21 @@ struct ItemCursor {
   int b, p, y;     // sequence, partition, head chunk
   int L;           // context length of b
   int t0, end;     // current stage start, end of the item's tokens
-  int full_left;   // full partitions still to visit after the current item
-  int round;       // next round of the partial deal
 };
 
-// Wave-uniform description of the deal.  The per-sequence size classes and
-// the per-class item counts live in LDS, so that looking up the next item
-// never issues a vector load (it would wait behind the K/V stream).
+// Wave-uniform description of the deal.  Per-sequence tables live in LDS, so
+// that finding an item never issues a vector load (it would wait behind the
+// K/V stream).
 struct Deal {
   int B, Y, P, W, w;
-  bool cls_in_lds;  // s_deal_cls holds the batch (else classes are recomputed)
+  long n_full;      // full partitions
+  int n_partial;    // partial partitions
+  bool in_lds;      // the LDS tables below hold the batch
 };
-__shared__ uint8_t s_deal_cls[kMaxDealSeqs];  // size class of each sequence
-__shared__ int s_deal_cnt[kSizeClasses];      // partial items per class, largest first
+__shared__ uint8_t s_deal_cls[kMaxDealSeqs];    // size class of each sequence's partial partition
+__shared__ uint16_t s_deal_full[kMaxDealSeqs];  // full partitions of each sequence
+__shared__ int s_deal_chunk[kMaxDealSeqs / 64];  // full items before each 64-sequence chunk
+__shared__ int s_deal_cnt[kSizeClasses];        // partial items per class, largest first
 
 // `lens` is the same array as a.context_lens, passed as a __restrict__
 // kernel argument: the kernel never writes it, so its reads can be scalar
@@ -459,10 +475,11 @@ __device__ __forceinline__ void cursor_begin(ItemCursor& k, int P) {
   k.end = min(k.L, k.t0 + P);
 }
 
-// Full partition of rank `target` (in (b, y, p) order).
-__device__ __forceinline__ void seek_full(ItemCursor& k, long target, const Deal& d,
-                                          const RowAttnArgs& a,
-                                          const int32_t* __restrict__ lens, int lane) {
+// Full partition of rank `target`, from the lengths (before the stream starts
+// or when the batch is too large for the LDS tables).
+__device__ __forceinline__ void seek_full_scan(ItemCursor& k, long target, const Deal& d,
+                                               const RowAttnArgs& a,
+                                               const int32_t* __restrict__ lens, int lane) {
   long acc = 0;
   k.b = d.B;
   int off = 0;
@@ -485,6 +502,32 @@ __device__ __forceinline__ void seek_full(ItemCursor& k, long target, const Deal
   k.L = seq_len(a, lens, k.b);
   const int nf = max(full_parts(k.L, d.P), 1);
   off = __builtin_amdgcn_readfirstlane(off);
+  k.y = off / nf;
+  k.p = off % nf;
+  cursor_begin(k, d.P);
+}
+
+// The same from the LDS tables: one ballot over the chunk prefixes, one scan
+// inside the chunk.
+__device__ __forceinline__ void seek_full_lds(ItemCursor& k, long target, const Deal& d,
+                                              const RowAttnArgs& a,
+                                              const int32_t* __restrict__ lens, int lane) {
+  const int nchunks = (d.B + 63) >> 6;
+  const int t = (int)target;  // n_full < 2^31 whenever the tables are used
+  const int pref = lane < nchunks ? s_deal_chunk[lane] : 0x7fffffff;
+  const unsigned long long le = __ballot(pref <= t);
+  const int ch = __builtin_amdgcn_readfirstlane(63 - (int)__builtin_clzll(le));
+  const int cbase = __builtin_amdgcn_readfirstlane(__shfl(pref, ch));
+  const int b = ch * 64 + lane;
+  const int ni = b < d.B ? d.Y * (int)s_deal_full[b] : 0;
+  const int incl = wave_scan(ni, lane);
+  const unsigned long long hit = __ballot(cbase + incl > t);
+  const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+  const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
+  k.b = ch * 64 + l0;
+  k.L = seq_len(a, lens, k.b);
+  const int nf = max(full_parts(k.L, d.P), 1);
+  const int off = t - cbase - excl;
   k.y = off / nf;
   k.p = off % nf;
   cursor_begin(k, d.P);
@@ -529,8 +572,8 @@ __device__ __forceinline__ void seek_partial(ItemCursor& k, int j, const Deal& d
   int seen = 0;
   for (int base = 0; base < d.B; base += 64) {
     const int b = base + lane;
-    const bool in = b < d.B && (d.cls_in_lds ? (int)s_deal_cls[b]
-                                             : tail_class(min(lens[b], a.max_context), d.P)) == c;
+    const bool in = b < d.B && (d.in_lds ? (int)s_deal_cls[b]
+                                         : tail_class(min(lens[b], a.max_context), d.P)) == c;
     const unsigned long long m = __ballot(in);
     const int n = __popcll(m);
     if (bi < seen + n) {
@@ -548,14 +591,17 @@ __device__ __forceinline__ void seek_partial(ItemCursor& k, int j, const Deal& d
   cursor_begin(k, d.P);
 }
 
-__device__ __forceinline__ void cursor_next_item(ItemCursor& k, const Deal& d,
-                                                 const RowAttnArgs& a,
-                                                 const int32_t* __restrict__ lens, int lane) {
-  if (k.full_left > 0) {
-    --k.full_left;
-    next_full(k, d, a, lens);
+// Cursor of item `code` (see the numbering above); `prev` is the cursor of
+// item code - 1 when the caller has it (then a full item is one step on).
+__device__ __forceinline__ void seek_item(ItemCursor& k, long code, bool follows,
+                                          const Deal& d, const RowAttnArgs& a,
+                                          const int32_t* __restrict__ lens, int lane) {
+  if (code < d.n_full) {
+    if (follows) next_full(k, d, a, lens);
+    else if (d.in_lds) seek_full_lds(k, code, d, a, lens, lane);
+    else seek_full_scan(k, code, d, a, lens, lane);
   } else {
-    seek_partial(k, partial_rank(d, k.round++), d, a, lens, lane);
+    seek_partial(k, (int)(code - d.n_full), d, a, lens, lane);
   }
 }
 
@@ -578,51 +624,98 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
   d.w = blockIdx.x;
   const int B = d.B, P = d.P, Y = d.Y;
 
-  // Full partitions and partial-partition classes over the batch; wave 0
-  // also zeroes rows whose length violates the precondition (no item covers
-  // them).
+  // Full partitions and partial-partition classes over the batch, and the
+  // LDS tables; wave 0 also zeroes rows whose length violates the
+  // precondition (no item covers them).  Lengths are read eight chunks of 64
+  // at a time, so their loads are in flight together.
   long n_full = 0;
-  d.cls_in_lds = B <= kMaxDealSeqs;
+  d.in_lds = B <= kMaxDealSeqs;
   if (lane < kSizeClasses) s_deal_cnt[lane] = 0;
-  int n_partial = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int b = base + lane;
-    const int L = b < B ? min(lens[b], a.max_context) : 1;
-    if (d.w == 0 && L <= 0)
-      for (int i = 0; i < a.num_q_heads * D; ++i)
-        E::store(reinterpret_cast<T*>(a.out) + (long)b * a.num_q_heads * D + i, 0.f);
-    n_full += (long)Y * __builtin_amdgcn_readfirstlane(wave_sum(b < B ? full_parts(L, P) : 0));
-    const int cls = b < B ? tail_class(L, P) : 0;
-    if (d.cls_in_lds && b < B) s_deal_cls[b] = (uint8_t)cls;
-    // Lane i counts class kSizeClasses - i.
-    int cnt = 0;
+  __syncthreads();
+  constexpr int kUnroll = 8;
+  for (int base0 = 0; base0 < B; base0 += 64 * kUnroll) {
+    int Lr[kUnroll];
 #pragma unroll
-    for (int i = 0; i < kSizeClasses; ++i) {
-      const int n = Y * __popcll(__ballot(cls == kSizeClasses - i));
-      cnt = lane == i ? n : cnt;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int b = base0 + u * 64 + lane;
+      Lr[u] = b < B ? min(lens[b], a.max_context) : 1;
     }
-    if (lane < kSizeClasses) s_deal_cnt[lane] += cnt;
-    n_partial += __builtin_amdgcn_readfirstlane(wave_sum(lane < kSizeClasses ? cnt : 0));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int base = base0 + u * 64;
+      if (base >= B) break;
+      const int b = base + lane;
+      const int L = Lr[u];
+      if (d.w == 0 && L <= 0)
+        for (int i = 0; i < a.num_q_heads * D; ++i)
+          E::store(reinterpret_cast<T*>(a.out) + (long)b * a.num_q_heads * D + i, 0.f);
+      const int fp = b < B ? full_parts(L, P) : 0;
+      const int cls = b < B ? tail_class(L, P) : 0;
+      if (d.in_lds) {
+        if (b < B) {
+          s_deal_cls[b] = (uint8_t)cls;
+          s_deal_full[b] = (uint16_t)min(fp, 0xffff);
+        }
+        if (lane == 0) s_deal_chunk[base >> 6] = (int)min(n_full, 0x7fffffffL);
+      }
+      if (cls > 0) atomicAdd(&s_deal_cnt[kSizeClasses - cls], Y);
+      n_full += (long)Y * __builtin_amdgcn_readfirstlane(wave_sum(fp));
+    }
   }
   __syncthreads();
+  const int n_partial =
+      __builtin_amdgcn_readfirstlane(wave_sum(lane < kSizeClasses ? s_deal_cnt[lane] : 0));
+  d.n_full = n_full;
+  d.n_partial = n_partial;
+  // The LDS tables serve lookups only while every count fits them.
+  d.in_lds = d.in_lds && n_full < 0x7fffffffL && a.max_context / P < 0xffff;
+  const bool dyn = a.ticket != nullptr && d.in_lds;
+  const long n_items = n_full + n_partial;
 
-  // This wave's run of full partitions, then its share of the partials.
-  const long fa = n_full / d.W, frem = n_full % d.W;
+  // This wave's static run of full partitions (of the first n_static), then
+  // tickets or its share of the partial snake.
+  const long n_static = dyn ? n_full * kStaticPct / 100 : n_full;
+  const long fa = n_static / d.W, frem = n_static % d.W;
   const long f0 = d.w < frem ? d.w * (fa + 1) : frem * (fa + 1) + (d.w - frem) * fa;
   const int nfull_w = (int)(d.w < frem ? fa + 1 : fa);
   const int rounds = n_partial / d.W, prem = n_partial % d.W;
-  const int npart_w = rounds + (((rounds & 1) ? d.w : d.W - 1 - d.w) < prem ? 1 : 0);
-  int left = nfull_w + npart_w;
-  if (left <= 0) return;
+  const int npart_w =
+      dyn ? 0 : rounds + (((rounds & 1) ? d.w : d.W - 1 - d.w) < prem ? 1 : 0);
 
-  ItemCursor cp;
-  cp.round = 0;
+  // Loader state: its cursor and item code, the static items still to
+  // visit after the current one, and the next snake round.  A ticket is
+  // taken when the loader reaches the last stage of its last assigned item,
+  // one stage before it is needed: late enough that the item goes to a wave
+  // that is about to be free, early enough that the atomic's latency hides
+  // behind that stage.
+  ItemCursor ld;
+  long ld_code;
+  int ld_full_left = 0, ld_round = 0;
+  unsigned tk = 0;
+  // The draw that returns this value is the last one of the launch.
+  const unsigned last_draw = (unsigned)(n_items - n_static) + (unsigned)d.W - 1u;
+  auto past_end = [&](unsigned t) __attribute__((always_inline)) {
+    if (t == last_draw && lane == 0)
+      __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   if (nfull_w > 0) {
-    cp.full_left = nfull_w - 1;
-    seek_full(cp, f0, d, a, lens, lane);
+    ld_full_left = nfull_w - 1;
+    ld_code = f0;
+    if (d.in_lds) seek_full_lds(ld, f0, d, a, lens, lane);
+    else seek_full_scan(ld, f0, d, a, lens, lane);
+  } else if (dyn) {
+    if (lane == 0) tk = atomicAdd(a.ticket, 1u);
+    const unsigned t = __builtin_amdgcn_readfirstlane(tk);
+    ld_code = n_static + (long)t;
+    if (ld_code >= n_items) {
+      past_end(t);
+      return;
+    }
+    seek_item(ld, ld_code, false, d, a, lens, lane);
   } else {
-    cp.full_left = 0;
-    seek_partial(cp, partial_rank(d, cp.round++), d, a, lens, lane);
+    if (npart_w <= 0) return;
+    ld_code = n_full + partial_rank(d, ld_round++);
+    seek_partial(ld, (int)(ld_code - n_full), d, a, lens, lane);
   }
 
   const T* kc = reinterpret_cast<const T*>(a.k_cache);
@@ -638,7 +731,7 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
     lane_off[s] = (unsigned)(s * RPS + r) * row_bytes + (unsigned)(c * EPL * sizeof(T));
 
   // Query rows of an item's HG heads.
-  auto load_q = [&](uint4 (&raw)[HG], const ItemCursor& k) {
+  auto load_q = [&](uint4 (&raw)[HG], const ItemCursor& k) __attribute__((always_inline)) {
     const int h0 = (k.y / a.head_chunks) * a.group + (k.y % a.head_chunks) * HG;
     const T* qp = reinterpret_cast<const T*>(a.q) + ((long)k.b * a.num_q_heads + h0) * D +
                   c * EPL;
@@ -646,8 +739,10 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
     for (int h = 0; h < HG; ++h) raw[h] = *reinterpret_cast<const uint4*>(qp + h * D);
   };
 
-  // One stage of the loader's item through a descriptor over its valid rows.
-  auto load = [&](uint4 (&kr)[SS], uint4 (&vr)[SS], const ItemCursor& k) {
+  // One stage of the loader's item through a descriptor over its valid rows;
+  // an item's first stage also brings its query rows.
+  auto load = [&](uint4 (&kr)[SS], uint4 (&vr)[SS], uint4 (&qr)[HG], const ItemCursor& k)
+      __attribute__((always_inline)) {
     const int g = k.y / a.head_chunks;
     const int blk =
         clamp_block(tables[(long)k.b * a.max_blocks_per_seq + (k.t0 >> bs_log2)], nb);
@@ -655,59 +750,89 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
     const unsigned bytes = (unsigned)min(k.end - k.t0, SUB) * row_bytes;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + base, bytes);
+    if (k.t0 == k.p * P) load_q(qr, k);
 #pragma unroll
     for (int s = 0; s < SS; ++s) kr[s] = buffer_load16(rk, lane_off[s]);
 #pragma unroll
     for (int s = 0; s < SS; ++s) vr[s] = buffer_load16(rv, lane_off[s]);
   };
 
-  // The loader runs NBUF - 1 stages ahead of the fold; once its last item's
-  // last stage is issued it keeps re-reading that stage (cached, unused).
-  ItemCursor ld = cp;
-  int ld_left = left;
-  auto ld_advance = [&]() {
+  // The loader runs NBUF - 1 stages ahead of the fold.  After its last item's
+  // last stage it keeps re-reading that stage (cached, unused) with code -1.
+  bool ld_done = false;
+  auto take_ticket = [&]() __attribute__((always_inline)) {
+    if (dyn && ld_full_left == 0 && ld.t0 + SUB >= ld.end && lane == 0)
+      tk = atomicAdd(a.ticket, 1u);
+  };
+  auto ld_advance = [&]() __attribute__((always_inline)) {
+    if (ld_done) return;
     if (ld.t0 + SUB < ld.end) {
       ld.t0 += SUB;
-    } else if (ld_left > 1) {
-      --ld_left;
-      cursor_next_item(ld, d, a, lens, lane);
+      take_ticket();
+      return;
+    }
+    if (ld_full_left > 0) {
+      --ld_full_left;
+      ++ld_code;
+      next_full(ld, d, a, lens);
+      take_ticket();
+    } else if (dyn) {
+      const unsigned t = __builtin_amdgcn_readfirstlane(tk);
+      const long next = n_static + (long)t;
+      if (next >= n_items) {
+        past_end(t);
+        ld_done = true;
+        return;
+      }
+      seek_item(ld, next, next == ld_code + 1, d, a, lens, lane);
+      ld_code = next;
+      take_ticket();
+    } else if (ld_round < npart_w) {
+      ld_code = n_full + partial_rank(d, ld_round++);
+      seek_partial(ld, (int)(ld_code - n_full), d, a, lens, lane);
+    } else {
+      ld_done = true;
     }
   };
 
-  F st;
-  {
-    uint4 qraw[HG];
-    load_q(qraw, cp);
-    st.set_q(qraw, a.scale_log2);
-  }
-  st.reset();
-
-  uint4 kbuf[NBUF][SS], vbuf[NBUF][SS];
+  // Register stages, each tagged with the item code and the first token of
+  // the stage it holds (-1: past the end).
+  take_ticket();
+  uint4 kbuf[NBUF][SS], vbuf[NBUF][SS], qbuf[NBUF][HG];
+  long slot_code[NBUF];
+  int slot_t0[NBUF];
+  ItemCursor cp = ld;
+  long cp_code = ld_code;
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i) {
-    load(kbuf[i], vbuf[i], ld);
+    load(kbuf[i], vbuf[i], qbuf[i], ld);
+    slot_code[i] = ld_done ? -1 : ld_code;
+    slot_t0[i] = ld.t0;
     ld_advance();
   }
+
+  F st;
+  st.set_q(qbuf[0], a.scale_log2);
+  st.reset();
   for (;;) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
-      load(kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF], ld);
+      const int sl = (i + NBUF - 1) % NBUF;
+      load(kbuf[sl], vbuf[sl], qbuf[sl], ld);
+      slot_code[sl] = ld_done ? -1 : ld_code;
+      slot_t0[sl] = ld.t0;
       ld_advance();
       __builtin_amdgcn_sched_barrier(0);
-      st.fold(kbuf[i], vbuf[i], cp.t0, cp.end, r);
-      if (cp.t0 + SUB < cp.end) {
-        cp.t0 += SUB;
-      } else {
+      st.fold(kbuf[i], vbuf[i], slot_t0[i], cp.end, r);
+      if (slot_t0[i] + SUB >= cp.end) {
         const int h0 = (cp.y / a.head_chunks) * a.group + (cp.y % a.head_chunks) * HG;
         st.finish(a, (long)cp.b * a.num_q_heads + h0, num_parts(cp.L, P), cp.p, c, r);
-        if (--left == 0) goto done;
-        const int pb = cp.b, py = cp.y;
-        cursor_next_item(cp, d, a, lens, lane);
-        if (cp.b != pb || cp.y != py) {  // new query rows (about once per wave)
-          uint4 qraw[HG];
-          load_q(qraw, cp);
-          st.set_q(qraw, a.scale_log2);
-        }
+        const int nx = (i + 1) % NBUF;
+        const long next = slot_code[nx];
+        if (next < 0) goto done;
+        seek_item(cp, next, next == cp_code + 1, d, a, lens, lane);
+        cp_code = next;
+        st.set_q(qbuf[nx], a.scale_log2);
         st.reset();
       }
     }
@@ -718,27 +843,50 @@ done:
 
 // ---------------------------------------------------------------- combine
 
-// One block of D threads per (row, query head): rescale the partitions'
-// partial outputs to a common max and normalise.
+// One wave per (row, query head): rescale the partitions' partial outputs to
+// a common max and normalise.  Lane p holds partition p's (max, sum); each
+// lane owns D / 64 output elements.  The sums run over the partitions in
+// order, so the result does not depend on which wave folded which partition.
 template <typename E, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(RowAttnArgs a) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   typedef typename E::storage T;
+  constexpr int PER = D / 64;
   const long oh = blockIdx.x;
   const int row = (int)(oh / a.num_q_heads);
   const int L = min(a.context_lens[row], a.max_context);
   const int nparts = num_parts(L, a.part_tokens);
   if (nparts <= 1) return;
+  const int lane = threadIdx.x;
   const float* ml = a.ws_ml + oh * a.max_parts * 2;
+  const float* po = a.ws_o + oh * a.max_parts * D + lane * PER;
   float M = kNegBig;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  const float* po = a.ws_o + oh * a.max_parts * D + threadIdx.x;
-  float acc = 0.f, lsum = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float wg = fast_exp2(ml[2 * p] - M);
-    acc = fmaf(po[(long)p * D], wg, acc);
-    lsum = fmaf(ml[2 * p + 1], wg, lsum);
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const float m = p0 + lane < nparts ? ml[2 * (p0 + lane)] : kNegBig;
+    float mx = m;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    M = fmaxf(M, mx);
   }
-  E::store(reinterpret_cast<T*>(a.out) + oh * D + threadIdx.x, acc / lsum);
+  float acc[PER], lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int n = min(64, nparts - p0);
+    const bool in = lane < n;
+    const float wl = in ? fast_exp2(ml[2 * (p0 + lane)] - M) : 0.f;
+    const float ll = in ? ml[2 * (p0 + lane) + 1] : 0.f;
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float wg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+      lsum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), j)), wg, lsum);
+      const float* pp = po + (long)(p0 + j) * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(pp[e], wg, acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    E::store(reinterpret_cast<T*>(a.out) + oh * D + lane * PER + e, acc[e] / lsum);
 }
 
 // ---------------------------------------------------------------- launch
@@ -832,12 +980,12 @@ int launch_decode(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t str
     if (head_dim == 64)
       hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 64>), g, dim3(64), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 128>), g, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 128>), g, dim3(64), 0, stream, a);
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 64>), g, dim3(64), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 128>), g, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 128>), g, dim3(64), 0, stream, a);
   }
   return 0;
 }

@@ -161,13 +161,18 @@ int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void*
   return launch_status();
 }
 
+// The decode workspace starts with the persistent kernel's work counter, at
+// a fixed place whatever the sizes of the call.
+constexpr size_t kCounterBytes = 256;
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
   const size_t parts = ((size_t)max_context_len + pa::kMinPartition - 1) / pa::kMinPartition;
   const size_t heads = (size_t)num_seqs * num_q_heads;
+  // [work counter: 256 B][partial outputs][partial max / sum]
   const size_t o_bytes = heads * parts * head_dim * sizeof(float);
-  const size_t ml_off = (o_bytes + 255) & ~(size_t)255;
+  const size_t ml_off = (kCounterBytes + o_bytes + 255) & ~(size_t)255;
   return ml_off + heads * parts * 2 * sizeof(float);
 }
 
@@ -239,9 +244,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
         ((size_t)max_context_len + pa::kMinPartition - 1) / pa::kMinPartition;
     const size_t heads = (size_t)num_seqs * num_q_heads;
     const size_t o_bytes = heads * parts_bound * head_dim * sizeof(float);
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       ((o_bytes + 255) & ~(size_t)255));
+    const size_t ml_off = (kCounterBytes + o_bytes + 255) & ~(size_t)255;
+    a.ticket = static_cast<unsigned*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off);
   }
   a.num_rows = num_seqs;
   a.num_seqs = num_seqs;

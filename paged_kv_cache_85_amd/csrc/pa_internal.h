@@ -28,6 +28,7 @@ struct RowAttnArgs {
   void* out;
   float* ws_o;                   // [rows, Hq, max_parts, D] unnormalised partial outputs
   float* ws_ml;                  // [rows, Hq, max_parts, 2] (running max in log2 units, sum)
+  unsigned* ticket;              // decode work counter in the workspace (null: static deal)
   int num_rows;
   int num_seqs;
   int num_q_heads;

@@ -50,7 +50,7 @@ class DecodeGraph:
         self.tables = torch.zeros(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.q)
         n = pa_decode_workspace_bytes(max_seqs, num_q_heads, d, max_context_len)
-        self.workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
         # One eager pass first (the library caches its occupancy queries on
         # the first launch, outside the capture), then the capture.
         side = torch.cuda.Stream(device=dev)

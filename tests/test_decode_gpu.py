@@ -105,9 +105,20 @@ def test_decode_workspace_reuse_and_too_small():
     need = pa.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
                                         case.max_context_len)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")   # stale NaN bytes
+    ws[:256] = 0                       # the work counter starts at zero ...
     out1, _, _ = run_decode(case, workspace=ws)
+    assert int(ws[:256].count_nonzero()) == 0   # ... and every call leaves it there
     out2, _, _ = run_decode(case, workspace=ws)
     assert np.array_equal(bits(out1), bits(out2))
+    big = make_case(3)                 # a larger call reusing the same counter
+    need3 = pa.pa_decode_workspace_bytes(big.num_seqs, big.num_q_heads, big.head_dim,
+                                         big.max_context_len)
+    ws3 = torch.full((need3,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    ws3[:256] = 0
+    r1, _, _ = run_decode(big, workspace=ws3)
+    r2, _, _ = run_decode(big, workspace=ws3)
+    assert int(ws3[:256].count_nonzero()) == 0
+    assert np.array_equal(bits(r1), bits(r2))
     with pytest.raises(pa.PAError) as e:
         run_decode(case, workspace=ws[: need // 2])
     assert e.value.status == pa.PA_E_WORKSPACE
