@@ -57,6 +57,40 @@ def test_decode_shapes_and_block_sizes(hq, hkv, d, dtype, bs):
     assert_close(f64(out), _oracle(case), dtype, spec.name + f" bs{bs}")
 
 
+def _sched_lens(kind):
+    rng = np.random.default_rng(5)
+    if kind == "over-4096-seqs":          # deal tables do not fit LDS: static snake
+        lens = rng.integers(1, 8, 4100, endpoint=True)
+        lens[rng.choice(4100, 100, replace=False)] = rng.integers(256, 320, 100, endpoint=True)
+        return lens, None
+    if kind == "one-partition":           # no workspace: static deal of partial items
+        return rng.integers(1, 256, 300, endpoint=True), 256
+    if kind == "full-only":               # no partial partitions
+        return 256 * rng.integers(1, 8, 200, endpoint=True), None
+    if kind == "partials-only-ticketed":  # workspace present, every item a ticketed partial
+        return rng.integers(1, 255, 300, endpoint=True), 1024
+    if kind == "few-items":               # fewer items than resident waves
+        return np.array([300, 1, 2048]), None
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["over-4096-seqs", "one-partition", "full-only",
+                                  "partials-only-ticketed", "few-items"])
+def test_decode_deal_paths(kind):
+    """The persistent kernel's ways of dealing items (blocks of 64 and 256
+    tokens): static snake, tickets, no full or no partial partitions, tiny
+    batches."""
+    lens, max_len = _sched_lens(kind)
+    bs = 64 if kind == "over-4096-seqs" else 256   # both take the persistent kernel
+    spec = DecodeSpec(f"deal-{kind}", 2, 1, 64, "bf16", bs, context_lens=tuple(int(x) for x in lens))
+    case = make_decode(spec, 13)
+    if max_len and max_len > case.max_context_len:
+        # a host bound above every length: the tables must cover it
+        case = decode_subset(case, range(len(lens)), table_width=-(-max_len // bs))
+    out, _, _ = run_decode(case, max_context_len=max_len or case.max_context_len)
+    assert_close(f64(out), _oracle(case), "bf16", f"deal {kind}")
+
+
 def test_decode_block_size_invariance_bitwise():
     """Paging changes addresses only: identical bits across block sizes."""
     spec = DecodeSpec("dec-bs-inv", 16, 8, 128, "bf16", 16,
