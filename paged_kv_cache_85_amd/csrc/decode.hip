@@ -183,6 +183,19 @@ struct RowFold {
     }
   }
 
+  // Max / sum over the RPS lane rows holding the same column c (lanes c,
+  // c + LPR, ...): pairwise steps at distances LPR, 2 LPR, ... 32.
+  __device__ static __forceinline__ float rows_max(float x) {
+    if constexpr (LPR <= 8) x = xor_max<8>(x);
+    if constexpr (LPR <= 16) x = xor_max<16>(x);
+    return xor_max<32>(x);
+  }
+  __device__ static __forceinline__ float rows_sum(float x) {
+    if constexpr (LPR <= 8) x = xor_sum<8>(x);
+    if constexpr (LPR <= 16) x = xor_sum<16>(x);
+    return xor_sum<32>(x);
+  }
+
   // Merge the RPS independent row states (lanes c, c + LPR, ...) and write
   // the item: normalised output when the sequence has one partition, else an
   // unnormalised partial.  Lanes of row 0 hold the merged state.
@@ -190,20 +203,11 @@ struct RowFold {
                                          int c, int r) {
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
-      float M = m[h];
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float M = rows_max(m[h]);
       const float wgt = fast_exp2(m[h] - M);
-      float lw = l[h] * wgt;
+      const float lw = rows_sum(l[h] * wgt);
 #pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float ov = o[h][e] * wgt;
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
-        o[h][e] = ov;
-      }
+      for (int e = 0; e < EPL; ++e) o[h][e] = rows_sum(o[h][e] * wgt);
       m[h] = M;
       l[h] = lw;
     }
@@ -487,11 +491,11 @@ __device__ __forceinline__ void seek_full_scan(ItemCursor& k, long target, const
     const int b = base + lane;
     const int ni = b < d.B ? d.Y * full_parts(min(lens[b], a.max_context), d.P) : 0;
     const int incl = wave_scan(ni, lane);
-    const int chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    const int chunk = __builtin_amdgcn_readlane(incl, 63);
     if (acc + chunk > target) {
       const unsigned long long hit = __ballot(acc + incl > target);
       const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
-      const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
+      const int excl = __builtin_amdgcn_readlane(incl - ni, l0);
       k.b = base + l0;
       off = (int)(target - acc - excl);
       break;
@@ -517,13 +521,13 @@ __device__ __forceinline__ void seek_full_lds(ItemCursor& k, long target, const 
   const int pref = lane < nchunks ? s_deal_chunk[lane] : 0x7fffffff;
   const unsigned long long le = __ballot(pref <= t);
   const int ch = __builtin_amdgcn_readfirstlane(63 - (int)__builtin_clzll(le));
-  const int cbase = __builtin_amdgcn_readfirstlane(__shfl(pref, ch));
+  const int cbase = __builtin_amdgcn_readlane(pref, ch);
   const int b = ch * 64 + lane;
   const int ni = b < d.B ? d.Y * (int)s_deal_full[b] : 0;
   const int incl = wave_scan(ni, lane);
   const unsigned long long hit = __ballot(cbase + incl > t);
   const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
-  const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - ni, l0));
+  const int excl = __builtin_amdgcn_readlane(incl - ni, l0);
   k.b = ch * 64 + l0;
   k.L = seq_len(a, lens, k.b);
   const int nf = max(full_parts(k.L, d.P), 1);
@@ -861,10 +865,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   const float* po = a.ws_o + oh * a.max_parts * D + lane * PER;
   float M = kNegBig;
   for (int p0 = 0; p0 < nparts; p0 += 64) {
-    const float m = p0 + lane < nparts ? ml[2 * (p0 + lane)] : kNegBig;
-    float mx = m;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float mx = p0 + lane < nparts ? ml[2 * (p0 + lane)] : kNegBig;
+    mx = xor_max<32>(mx);
+    mx = xor_max<16>(mx);
+    mx = xor_max<8>(mx);
+    mx = xor_max<4>(mx);
+    mx = xor_max<2>(mx);
+    mx = xor_max<1>(mx);
     M = fmaxf(M, mx);
   }
   float acc[PER], lsum = 0.f;

@@ -37,11 +37,53 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+// Lane i together with lane i ^ OFF (OFF = 16 or 32) through the gfx950
+// lane-swap instructions, register to register: swapping x with itself
+// leaves, in every lane, x of the lower-numbered partner in `a` and x of the
+// higher-numbered one in `b`.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  static_assert(OFF == 16 || OFF == 32, "swap distance");
+  const unsigned u = __float_as_uint(x);
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// x combined with x of lane i ^ OFF (OFF a power of two below 64): the same
+// two operands as x + __shfl_xor(x, OFF) (or the max), so the same bits.
+template <int OFF>
+__device__ __forceinline__ float xor_sum(float x) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    float a, b;
+    lane_pair<OFF>(x, a, b);
+    return a + b;
+  } else {
+    return x + __shfl_xor(x, OFF);
+  }
+}
+template <int OFF>
+__device__ __forceinline__ float xor_max(float x) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    float a, b;
+    lane_pair<OFF>(x, a, b);
+    return fmaxf(a, b);
+  } else {
+    return fmaxf(x, __shfl_xor(x, OFF));
+  }
+}
+
 // Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of a group
 // receives the group total.  After the two quad steps each quad holds its own
 // sum; the half-row mirror pairs the two quads of an 8-lane half; the row
 // mirror pairs the two halves of a 16-lane row; a 32-lane group adds the
-// neighbouring row through ds_swizzle/bpermute.
+// neighbouring row with a lane swap.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   static_assert(N == 8 || N == 16 || N == 32, "group size");
@@ -49,7 +91,7 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dpp<DPP_QUAD_2301>(x);
   x += dpp<DPP_ROW_HALF_MIRROR>(x);
   if constexpr (N >= 16) x += dpp<DPP_ROW_MIRROR>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 32) x = xor_sum<16>(x);
   return x;
 }
 
