@@ -63,7 +63,7 @@ enum {
   PA_OK = 0,
   PA_E_INVAL = -1,        /* null pointer, bad size, Hq % Hkv != 0, bad index data */
   PA_E_UNSUPPORTED = -2,  /* head_dim or dtype outside what the kernels cover */
-  PA_E_WORKSPACE = -3,    /* decode workspace too small */
+  PA_E_WORKSPACE = -3,    /* workspace too small */
   PA_E_HIP = -4,          /* HIP runtime error while launching */
   PA_E_NOMEM = -5         /* block manager: not enough free blocks (nothing changed) */
 };
@@ -128,6 +128,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* Workspace bytes pa_prefill_varlen takes (its work counter). */
+#define PA_PREFILL_WORKSPACE_BYTES 256
+
 /*
  * Varlen causal prefill.  Sequence b owns query rows
  * [cu_seqlens_q[b], cu_seqlens_q[b+1]) (Lq of them) and Lk =
@@ -142,7 +145,16 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   cu_seqlens_q, cu_seqlens_k  int32 [num_seqs + 1]
  *   max_seqlen_q, max_seqlen_k  host upper bounds of Lq and Lk
  *   head_dim      64 or 128
- * bf16 runs on the matrix cores; fp32 runs on the vector ALUs.
+ *   workspace     NULL, or device memory of at least PA_PREFILL_WORKSPACE_BYTES
+ *                 bytes, 256-byte aligned, holding a work counter that must be
+ *                 zero before the first call that uses the memory (every call
+ *                 leaves it zero).  With it, the query tiles left after each
+ *                 workgroup's first go to whichever workgroup is free; without
+ *                 it they are dealt in a fixed order.  Results are bitwise the
+ *                 same either way.  Calls that run concurrently need
+ *                 workspaces of their own.  PA_E_WORKSPACE if too small.
+ * bf16 runs on the matrix cores; fp32 runs on the vector ALUs (and ignores
+ * the workspace).
  * num_seqs == 0 or total_q == 0 is a no-op.
  */
 int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -151,7 +163,8 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float scale,
-                      int32_t dtype, void* stream);
+                      int32_t dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * Store prologue: normalise and rotate the new tokens' queries and keys, then

@@ -49,7 +49,7 @@ def lib() -> ctypes.CDLL:
                                 f32, i32, vp, sz, vp]
         L.pa_decode.restype = ctypes.c_int
         L.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                        i32, i32, i32, i32, f32, i32, vp]
+                                        i32, i32, i32, i32, f32, i32, vp, sz, vp]
         L.pa_prefill_varlen.restype = ctypes.c_int
         L.pa_qk_norm_rope_store.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                             i32, i32, i32, i32, i32, f32, i32, vp]
@@ -173,9 +173,29 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     _check("pa_decode", rc)
 
 
+PREFILL_WORKSPACE_BYTES = 256
+_prefill_ws = {}
+
+
+def prefill_workspace(device, stream=None):
+    """The zeroed work counter pa_prefill_varlen uses on (device, stream) when
+    the caller passes none: one per stream, since calls on one stream run in
+    order and each leaves the counter zero."""
+    torch = _torch()
+    key = (torch.device(device).index or 0, _stream(stream) or 0)
+    ws = _prefill_ws.get(key)
+    if ws is None:
+        ws = torch.zeros(PREFILL_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+        _prefill_ws[key] = ws
+    return ws
+
+
 def pa_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
-                      max_seqlen_q: int, max_seqlen_k: int, scale: float, stream=None) -> None:
-    """q, out: [Tq, Hq, D] packed; cu_seqlens_q/k: int32 [B + 1]; block_tables: int32 [B, MB]."""
+                      max_seqlen_q: int, max_seqlen_k: int, scale: float, workspace=None,
+                      stream=None) -> None:
+    """q, out: [Tq, Hq, D] packed; cu_seqlens_q/k: int32 [B + 1]; block_tables: int32 [B, MB].
+    workspace: a device tensor of PREFILL_WORKSPACE_BYTES zeroed before its first use
+    (None: one cached per stream; False: none, items dealt in a fixed order)."""
     torch = _torch()
     dt = _dtype_code(q)
     tq, hq, d = q.shape
@@ -186,6 +206,10 @@ def pa_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_s
     if cu_seqlens_k.shape != cu_seqlens_q.shape or block_tables.dim() != 2 or \
             block_tables.shape[0] != B:
         raise ValueError("cu_seqlens must be [B + 1] and block_tables [B, MB]")
+    if workspace is None:
+        workspace = prefill_workspace(q.device, stream)
+    ws_ptr, ws_bytes = (None, 0) if workspace is False else (
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
     rc = lib().pa_prefill_varlen(_ptr(out, "out", q.dtype), _ptr(q, "q"),
                                  _ptr(k_cache, "k_cache", q.dtype),
                                  _ptr(v_cache, "v_cache", q.dtype),
@@ -193,7 +217,8 @@ def pa_prefill_varlen(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_s
                                  _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
                                  _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, tq,
                                  int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, nb, bs,
-                                 block_tables.shape[1], float(scale), dt, _stream(stream))
+                                 block_tables.shape[1], float(scale), dt, ws_ptr, ws_bytes,
+                                 _stream(stream))
     _check("pa_prefill_varlen", rc)
 
 

@@ -64,7 +64,7 @@ const char* pa_status_string(int status) {
     case PA_OK: return "ok";
     case PA_E_INVAL: return "invalid argument";
     case PA_E_UNSUPPORTED: return "unsupported head_dim, dtype or shape";
-    case PA_E_WORKSPACE: return "decode workspace too small";
+    case PA_E_WORKSPACE: return "workspace too small";
     case PA_E_HIP: return "HIP runtime error";
     case PA_E_NOMEM: return "not enough free blocks";
     default: return "unknown status";
@@ -274,7 +274,8 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float scale,
-                      int32_t dtype, void* stream) {
+                      int32_t dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
       num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 || block_size < 1 ||
       max_blocks_per_seq < 1 || !isfinite(scale) || !(scale > 0.f))
@@ -285,6 +286,10 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
   if (max_seqlen_q > max_seqlen_k) return PA_E_INVAL;
   if ((long long)max_blocks_per_seq * block_size < max_seqlen_k) return PA_E_INVAL;
   if ((long long)num_blocks * block_size > INT32_MAX) return PA_E_INVAL;
+  if (workspace) {
+    if (workspace_bytes < PA_PREFILL_WORKSPACE_BYTES) return PA_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_E_INVAL;
+  }
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
     return PA_E_INVAL;
@@ -323,6 +328,7 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
     a.block_size = block_size;
     a.block_size_log2 = log2_exact(block_size);
     a.scale_log2 = (float)((double)scale * kLog2e);
+    a.ticket = static_cast<unsigned*>(workspace);
     if (pa::launch_prefill_bf16(a, head_dim, s)) return PA_E_UNSUPPORTED;
     return launch_status();
   }

@@ -69,7 +69,8 @@ struct PrefillArgs {
   int block_size;
   int block_size_log2;
   float scale_log2;
-  int persistent;  // set by the launcher: workgroups loop over work items
+  int persistent;   // set by the launcher: workgroups loop over work items
+  unsigned* ticket; // work counter (null: every item dealt in a fixed order)
 };
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);

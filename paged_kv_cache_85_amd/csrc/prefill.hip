@@ -210,13 +210,24 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   // is query tile n_qt - 1 - qt_rev of sequence b, KV head / head chunk gh;
   // tiles past a sequence's end are empty.  A launch with one workgroup per
   // item maps blockIdx to its item.  A persistent launch (one workgroup per
-  // resident slot) walks the non-empty items in that order and takes those
-  // whose rank k among them is r * G + i (r even) or r * G + G - 1 - i (r odd)
-  // for workgroup i of G: a snake over a list sorted by decreasing cost,
-  // which evens out the total work per workgroup.
+  // resident slot) walks the non-empty items in that order.  Workgroup i of G
+  // first takes the item of rank i.  With a work counter, every later item
+  // goes to whichever workgroup asks first -- heaviest first to the first
+  // free workgroup, which evens out both the items' costs and the
+  // workgroups' unequal speeds; each workgroup draws its next rank a few
+  // tiles before its current item ends, so the draw's latency hides behind
+  // those tiles.  A launch of G workgroups makes exactly G draws past the
+  // end of the list, and the one that draws the last value puts the counter
+  // back to zero.  Without a counter the ranks are dealt in a snake: r * G + i
+  // (r even) or r * G + G - 1 - i (r odd).  Which workgroup computes an item
+  // never changes its arithmetic.
   __shared__ uint16_t s_ntiles[kMaxPersistSeqs];
+  __shared__ int s_items[4];
+  __shared__ unsigned s_ticket;
   const bool persistent = a.persistent != 0;
+  int n_items = 0;  // non-empty items (persistent launches)
   if (persistent) {
+    int mine = 0;
     for (int i = tid; i < num_seqs; i += 256) {
       const int qs = cu_q[i], qe = cu_q[i + 1], kl = cu_k[i + 1] - cu_k[i];
       int nq = 0;
@@ -226,17 +237,47 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
         nq = lq > 0 ? (lq + BMQ - 1) / BMQ : 0;
       }
       s_ntiles[i] = (uint16_t)nq;
+      mine += nq;
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
+    if (lane == 0) s_items[w] = mine;
     __syncthreads();
+    n_items = (s_items[0] + s_items[1] + s_items[2] + s_items[3]) * inner;
   }
   ItemWalk walk{0, 0, 0};
   const int G = gridDim.x;
   const int gi = blockIdx.x;
+  // Dynamic dealing needs every workgroup to hold a first item (each then
+  // draws until a draw comes back past the end).
+  const bool dyn = persistent && a.ticket != nullptr && n_items > G;
+  const unsigned last_draw = (unsigned)(n_items - G) + (unsigned)G - 1u;
+  unsigned tk = 0;     // thread 0: the rank drawn during the current item
+  bool drew = false;   // thread 0: whether that draw has been made
 
   for (int round = 0;; ++round) {
   int qt, b, gh;
   if (persistent) {
-    const int k = round * G + ((round & 1) ? G - 1 - gi : gi);
+    int k;
+    if (dyn && round > 0) {
+      // The rank drawn during the previous item (drawn now if that item
+      // ended before its draw point), published to the whole workgroup.
+      if (tid == 0) {
+        if (!drew) tk = atomicAdd(a.ticket, 1u);
+        s_ticket = tk;
+      }
+      __syncthreads();
+      const unsigned t = __builtin_amdgcn_readfirstlane(s_ticket);
+      drew = false;
+      if ((long)G + t >= (long)n_items) {
+        if (t == last_draw && tid == 0)
+          __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      k = G + (int)t;
+    } else {
+      k = round * G + ((round & 1) ? G - 1 - gi : gi);
+    }
     if (!walk_to(walk, k, s_ntiles, num_seqs, n_qt, inner, lane, qt, b, gh)) break;
   } else {
     if (round > 0) break;
@@ -268,6 +309,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   const int kmax_wave = delta + min(row0 + 32, Lq) - 1;
   const int kmax_wg = delta + min(qt * BMQ + BMQ, Lq) - 1;
   const int n_tiles = kmax_wg / BN + 1;
+  const int draw_kt = max(0, n_tiles - 3);  // tile step at which the next rank is drawn
 
   bf16x8 qB[KC];
   const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
@@ -459,6 +501,13 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     uint16_t* nk = st[(S + NST - 1) % NST];
     uint16_t* sv = sk + BN * D;
     uint16_t* nv = nk + BN * D;
+    // (The draw is one more vector-memory operation in flight for wave 0;
+    // the tile waits below then wait for one operation more than needed,
+    // never fewer, since operations complete in issue order.)
+    if (dyn && tid == 0 && kt == draw_kt) {
+      tk = atomicAdd(a.ticket, 1u);
+      drew = true;
+    }
     if constexpr (DMA) {
       wait_tiles<2 * NI, NST - 2>(min(NST - 2, n_tiles - 1 - kt));
       asm volatile("" ::: "memory");

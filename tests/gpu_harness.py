@@ -80,7 +80,9 @@ def run_decode(case, store: bool = True, workspace=None, max_context_len=None):
     return out, kc, vc
 
 
-def run_prefill(case, store: bool = True):
+def run_prefill(case, store: bool = True, workspace=None):
+    """Store then prefill on the GPU; `workspace` as in pa_prefill_varlen
+    (None: the binding's per-stream work counter; False: none)."""
     from paged_kv_cache_85_amd import pa_prefill_varlen
     say(f"prefill {case.spec.name}: B={case.num_seqs} Tq={case.total_q} "
         f"Tk={int(case.cu_seqlens_k[-1])} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
@@ -93,7 +95,7 @@ def run_prefill(case, store: bool = True):
     out = empty_like_rows(q.shape, case.dtype)
     pa_prefill_varlen(out, q, kc, vc, dev(case.block_tables), dev(case.cu_seqlens_q),
                       dev(case.cu_seqlens_k), case.max_seqlen_q, case.max_seqlen_k,
-                      float(case.scale))
+                      float(case.scale), workspace=workspace)
     torch().cuda.synchronize()
     return out, kc, vc
 

@@ -81,11 +81,13 @@ def test_decode_validation(lib):
 
 def _prefill(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cq=FAKE, ck=FAKE, B=3, tq=30, mq=20,
-             mk=40, hq=16, hkv=8, d=128, nb=64, bs=16, mb=4, scale=0.1, dtype=1, stream=None)
+             mk=40, hq=16, hkv=8, d=128, nb=64, bs=16, mb=4, scale=0.1, dtype=1, ws=None,
+             wsb=0, stream=None)
     a.update(kw)
     return lib.pa_prefill_varlen(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cq"], a["ck"],
                                  a["B"], a["tq"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"],
-                                 a["nb"], a["bs"], a["mb"], a["scale"], a["dtype"], a["stream"])
+                                 a["nb"], a["bs"], a["mb"], a["scale"], a["dtype"], a["ws"],
+                                 a["wsb"], a["stream"])
 
 
 def test_prefill_validation(lib):
@@ -97,6 +99,9 @@ def test_prefill_validation(lib):
     assert _prefill(lib, scale=-1.0) == pa.PA_E_INVAL
     assert _prefill(lib, tq=0) == pa.PA_OK
     assert _prefill(lib, B=0) == pa.PA_OK
+    assert _prefill(lib, ws=FAKE, wsb=16) == pa.PA_E_WORKSPACE     # counter area too small
+    assert _prefill(lib, ws=ctypes.c_void_p(0x1010), wsb=256) == pa.PA_E_INVAL   # unaligned
+    assert binding.PREFILL_WORKSPACE_BYTES == 256
 
 
 def test_store_validation(lib):

@@ -59,6 +59,21 @@ def test_prefill_poison(poison):
     assert_close(f64(out), _oracle(case), "bf16", f"prefill poison {poison}")
 
 
+@pytest.mark.parametrize("config", [4, 5])
+def test_prefill_work_counter_bitwise(config):
+    """Query tiles dealt through the work counter (whichever workgroup is
+    free) or in the fixed snake give the same bits, and every call leaves the
+    counter at zero."""
+    import torch
+    case = make_case(config)
+    fixed, _, _ = run_prefill(case, workspace=False)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda:0")
+    for rep in range(3):
+        dealt, _, _ = run_prefill(case, workspace=ws)
+        assert np.array_equal(bits(dealt), bits(fixed)), f"config {config} call {rep}"
+        assert int(ws.count_nonzero()) == 0, "the work counter must come back to zero"
+
+
 def test_prefill_invariance_bitwise():
     spec = PrefillSpec("pre-inv", 16, 8, 128, "bf16", 16, q_len_range=(1, 1),
                        q_lens=(40, 130, 1, 77), prefix_lens=(0, 20, 256, 5))
