@@ -871,21 +871,37 @@ done:
 // a common max and normalise.  Lane p holds partition p's (max, sum); each
 // lane owns D / 64 output elements.  The sums run over the partitions in
 // order, so the result does not depend on which wave folded which partition.
+// The row length, the first 64 partitions' (max, sum) and the first kPre
+// partitions' partial rows are requested together, before the length is
+// known (every index stays inside the row's max_parts workspace entries;
+// values past the row's partitions are never used), so that one memory
+// latency, not three, precedes the arithmetic.
+constexpr int kCombinePre = 8;
+
 template <typename E, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   typedef typename E::storage T;
   constexpr int PER = D / 64;
   const long oh = blockIdx.x;
   const int row = (int)(oh / a.num_q_heads);
-  const int L = min(a.context_lens[row], a.max_context);
-  const int nparts = num_parts(L, a.part_tokens);
-  if (nparts <= 1) return;
   const int lane = threadIdx.x;
   const float* ml = a.ws_ml + oh * a.max_parts * 2;
   const float* po = a.ws_o + oh * a.max_parts * D + lane * PER;
+  const int Lraw = a.context_lens[row];
+  float2 ml0 = make_float2(kNegBig, 0.f);
+  if (lane < a.max_parts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
+  float pre[kCombinePre][PER];
+#pragma unroll
+  for (int j = 0; j < kCombinePre; ++j)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[j][e] = j < a.max_parts ? po[(long)j * D + e] : 0.f;
+
+  const int L = min(Lraw, a.max_context);
+  const int nparts = num_parts(L, a.part_tokens);
+  if (nparts <= 1) return;
   float M = kNegBig;
   for (int p0 = 0; p0 < nparts; p0 += 64) {
-    float mx = p0 + lane < nparts ? ml[2 * (p0 + lane)] : kNegBig;
+    float mx = p0 + lane < nparts ? (p0 == 0 ? ml0.x : ml[2 * (p0 + lane)]) : kNegBig;
     mx = xor_max<32>(mx);
     mx = xor_max<16>(mx);
     mx = xor_max<8>(mx);
@@ -900,10 +916,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     const int n = min(64, nparts - p0);
     const bool in = lane < n;
-    const float wl = in ? fast_exp2(ml[2 * (p0 + lane)] - M) : 0.f;
-    const float ll = in ? ml[2 * (p0 + lane) + 1] : 0.f;
+    const float wl = in ? fast_exp2((p0 == 0 ? ml0.x : ml[2 * (p0 + lane)]) - M) : 0.f;
+    const float ll = in ? (p0 == 0 ? ml0.y : ml[2 * (p0 + lane) + 1]) : 0.f;
+    int j = 0;
+    if (p0 == 0) {
+#pragma unroll
+      for (; j < kCombinePre; ++j) {
+        if (j >= n) break;
+        const float wg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+        lsum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), j)), wg, lsum);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(pre[j][e], wg, acc[e]);
+      }
+    }
 #pragma unroll 8
-    for (int j = 0; j < n; ++j) {
+    for (; j < n; ++j) {
       const float wg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
       lsum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), j)), wg, lsum);
       const float* pp = po + (long)(p0 + j) * D;
