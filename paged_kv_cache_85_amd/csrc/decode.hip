@@ -709,9 +709,11 @@ __global__ __launch_bounds__(64) void decode_persistent_kernel(
   // Loader state: its cursor and item code, the static items still to
   // visit after the current one, and the next snake round.  A ticket is
   // taken when the loader reaches the last stage of its last assigned item,
-  // one stage before it is needed: late enough that the item goes to a wave
-  // that is about to be free, early enough that the atomic's latency hides
-  // behind that stage.
+  // one stage before it is needed, so that the item goes to a wave that is
+  // about to be free.  (The compiler emits the single-lane draw in a
+  // wave-aggregated form that reads its result at once, so the wave waits
+  // for the atomic and the stages in flight right there; compiling without
+  // that form measured slower.)
   ItemCursor ld;
   long ld_code;
   int ld_full_left = 0, ld_round = 0;

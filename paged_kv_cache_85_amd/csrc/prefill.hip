@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   // goes to whichever workgroup asks first -- heaviest first to the first
   // free workgroup, which evens out both the items' costs and the
   // workgroups' unequal speeds; each workgroup draws its next rank a few
-  // tiles before its current item ends, so the draw's latency hides behind
-  // those tiles.  A launch of G workgroups makes exactly G draws past the
+  // tiles before its current item ends (its first wave waits for the draw
+  // there: the compiler's wave-aggregated atomic reads the result at once).
+  // A launch of G workgroups makes exactly G draws past the
   // end of the list, and the one that draws the last value puts the counter
   // back to zero.  Without a counter the ranks are dealt in a snake: r * G + i
   // (r even) or r * G + G - 1 - i (r odd).  Which workgroup computes an item
