@@ -74,15 +74,23 @@ __device__ __forceinline__ u32x4 stream_rsrc(const void* base, unsigned bytes) {
 }
 
 // 16 bytes per lane from buffer offset voff straight into LDS: the wave's 64
-// lanes fill 1 KiB at dst (wave-uniform) in lane order.  Issued as inline
+// lanes fill 1 KiB at dst (wave-uniform) in lane order; NT adds the
+// non-temporal cache policy (gfx940-family bit NT).  Issued as inline
 // assembly so that the compiler does not add its own waits for it; the
 // caller orders it with vm_wait and barriers.
+template <bool NT>
 __device__ __forceinline__ void lds_load16(u32x4 rsrc, uint16_t* dst, unsigned voff) {
   const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
+  if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
 }
 
 // Wait until at most N vector-memory loads of this thread are outstanding
@@ -177,8 +185,10 @@ __device__ __forceinline__ bool walk_to(ItemWalk& wk, int k, const uint16_t* nti
   return false;
 }
 
-// BN keys per tile, NST tile stages in LDS.
-template <int D, int HPW, bool DMA, int BN, int NST>
+// BN keys per tile, NST tile stages in LDS.  NT: the tiles stream with the
+// non-temporal cache policy (launches of decode rows only, whose tiles are
+// read once).
+template <int D, int HPW, bool DMA, int BN, int NST, bool NT>
 __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k) {
@@ -344,9 +354,9 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     const u32x4 rk = stream_rsrc(kcache + base, bytes);
     const u32x4 rv = stream_rsrc(vcache + base, bytes);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16(rk, dk + (w * NI + i) * 512, src_off[i]);
+    for (int i = 0; i < NI; ++i) lds_load16<NT>(rk, dk + (w * NI + i) * 512, src_off[i]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16(rv, dv + (w * NI + i) * 512, src_off[i]);
+    for (int i = 0; i < NI; ++i) lds_load16<NT>(rv, dv + (w * NI + i) * 512, src_off[i]);
   };
 
   // Other block sizes: the same chunks through registers, each row looked up
@@ -597,7 +607,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   }
 }
 
-template <int D, int HPW, bool DMA>
+template <int D, int HPW, bool DMA, bool NT>
 static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t stream) {
   constexpr int BN = PA_PREFILL_BN;
   constexpr int NST = PA_PREFILL_NST;
@@ -611,7 +621,7 @@ static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t str
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return -1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(prefill_bf16_kernel<D, HPW, DMA, BN, NST>),
+            &per_cu, reinterpret_cast<const void*>(prefill_bf16_kernel<D, HPW, DMA, BN, NST, NT>),
             256, 0) != hipSuccess)
       return -1;
     cached_slots = max(1, cus * max(per_cu, 1));
@@ -622,7 +632,7 @@ static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t str
   p.persistent = (a.num_seqs <= kMaxPersistSeqs && a.max_seqlen_q < (1 << 21) &&
                   n_items > cached_slots) ? 1 : 0;
   const long long grid = p.persistent ? cached_slots : n_items;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST>), dim3((unsigned)grid), dim3(256),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST, NT>), dim3((unsigned)grid), dim3(256),
                      0, stream, p, a.block_tables, a.cu_seqlens_q, a.cu_seqlens_k);
   return 0;
 }
@@ -635,9 +645,15 @@ static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
       n_qt * a.num_seqs * (long long)a.num_kv_heads * (a.group / HPW);
   if (n_items <= 0) return 0;
   if (n_items > 0x7fffffffLL) return -1;
-  if (a.block_size_log2 >= 0 && (1 << a.block_size_log2) >= PA_PREFILL_BN)
-    return launch_items<D, HPW, true>(a, n_items, stream);  // tiles inside one block
-  return launch_items<D, HPW, false>(a, n_items, stream);
+  if (a.block_size_log2 >= 0 && (1 << a.block_size_log2) >= PA_PREFILL_BN) {
+    // Tiles inside one block.  When every query row is a decode row (one
+    // row per sequence), each key/value tile is read by a single item:
+    // those launches stream the tiles past the caches, as decode does; any
+    // longer query tile re-reads its sequence's tiles through L2.
+    if (a.max_seqlen_q == 1) return launch_items<D, HPW, true, true>(a, n_items, stream);
+    return launch_items<D, HPW, true, false>(a, n_items, stream);
+  }
+  return launch_items<D, HPW, false, false>(a, n_items, stream);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
