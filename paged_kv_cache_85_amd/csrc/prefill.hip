@@ -438,20 +438,21 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     // kt*BN + 32*nb + 16*(t/8) + 8*lh + t%8.
     const bool need_mask = (kt * BN + BN - 1 > delta + row0) || (kt * BN + BN > Lk);
     if (need_mask) {
+      // Key kt*BN + 8*lh + off is visible iff it is <= klim and < Lk, i.e.
+      // iff off <= min(klim, Lk - 1) - kt*BN - 8*lh.
+      const int thr = min(klim, Lk - 1) - (kt * BN + 8 * lh);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int key = kt * BN + 32 * nb + 16 * (t >> 3) + 8 * lh + (t & 7);
-          if (key > klim || key >= Lk) sacc[nb][t] = -INFINITY;
-        }
+        for (int t = 0; t < 16; ++t)
+          if (32 * nb + 16 * (t >> 3) + (t & 7) > thr) sacc[nb][t] = -INFINITY;
     }
     float mx = sacc[0][0];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) mx = fmaxf(mx, sacc[nb][t]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0: max commutes with it
+    mx = xor_max<32>(mx) * scale_log2;  // scale > 0: max commutes with it
     // Lazy rescale: the reference max m_run only moves when a row's max
     // exceeds it by more than 2^8 (so probabilities stay <= 256); the final
     // O / l is the same for any reference, and the O rescale is skipped for
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor_sum<32>(l_run);
   if (wave_active && my_row < Lq) {
     const float inv = 1.f / l_tot;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
