@@ -441,20 +441,37 @@ constexpr int kMaxDealSeqs = 4096;  // per-sequence deal tables kept in LDS up t
 #endif
 constexpr int kStaticPct = PA_DECODE_STATIC_PCT;  // full partitions dealt statically (percent)
 
-// Sum of x over the wave.
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// Integer DPP step: x of the lane selected by the GFX9 DPP control CTRL
+// (rows outside ROWS, and lanes whose source lies outside their row, read 0).
+template <int CTRL, int ROWS = 0xF, bool BC = true>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, BC);
 }
 
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+// Sum of x over the wave, register to register: the two quad permutes and
+// the two mirrors sum each 16-lane row, the lane swaps add rows 16 and 32
+// apart (no LDS round trips).
+__device__ __forceinline__ int wave_sum(int x) {
+  x += dpp_i32<DPP_QUAD_1032>(x);
+  x += dpp_i32<DPP_QUAD_2301>(x);
+  x += dpp_i32<DPP_ROW_HALF_MIRROR>(x);
+  x += dpp_i32<DPP_ROW_MIRROR>(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = (int)(r16[0] + r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)(r32[0] + r32[1]);
+}
+
+// Inclusive prefix sum over the wave: shifts by 1, 2, 4 and 8 lanes inside
+// each 16-lane row, then lane 15 of a row is added to the next row (rows 1
+// and 3) and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_scan(int x) {
+  x += dpp_i32<0x111>(x);        // row_shr:1
+  x += dpp_i32<0x112>(x);        // row_shr:2
+  x += dpp_i32<0x114>(x);        // row_shr:4
+  x += dpp_i32<0x118>(x);        // row_shr:8
+  x += dpp_i32<0x142, 0xA, false>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_i32<0x143, 0xC, false>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -510,7 +527,7 @@ __device__ __forceinline__ void seek_full_scan(ItemCursor& k, long target, const
   for (int base = 0; base < d.B; base += 64) {
     const int b = base + lane;
     const int ni = b < d.B ? d.Y * full_parts(min(lens[b], a.max_context), d.P) : 0;
-    const int incl = wave_scan(ni, lane);
+    const int incl = wave_scan(ni);
     const int chunk = __builtin_amdgcn_readlane(incl, 63);
     if (acc + chunk > target) {
       const unsigned long long hit = __ballot(acc + incl > target);
@@ -544,7 +561,7 @@ __device__ __forceinline__ void seek_full_lds(ItemCursor& k, long target, const 
   const int cbase = __builtin_amdgcn_readlane(pref, ch);
   const int b = ch * 64 + lane;
   const int ni = b < d.B ? d.Y * (int)s_deal_full[b] : 0;
-  const int incl = wave_scan(ni, lane);
+  const int incl = wave_scan(ni);
   const unsigned long long hit = __ballot(cbase + incl > t);
   const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
   const int excl = __builtin_amdgcn_readlane(incl - ni, l0);
