@@ -47,6 +47,8 @@
  *     returns PA_E_INVAL on a violation (this synchronises the stream).
  *   - scale (the softmax temperature applied to q.k) must be finite and > 0.
  *   - Outputs must not alias inputs; k/v must not alias the pools.
+ *   - pa_decode and pa_prefill_varlen move element rows in 16-byte pieces:
+ *     out, q and both pools must be 16-byte aligned (else PA_E_INVAL).
  *   - The library is stateless; calls on different streams may overlap.
  */
 #ifndef PA_H_

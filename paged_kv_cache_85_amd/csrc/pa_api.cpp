@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -56,6 +57,13 @@ int launch_status() {
 }
 
 }  // namespace
+
+// The attention kernels move element rows in whole 16-byte pieces.
+static bool rows_aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
 
 extern "C" {
 
@@ -209,6 +217,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if ((long long)num_blocks * block_size > INT32_MAX) return PA_E_INVAL;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_E_INVAL;
+  if (!rows_aligned16({out, q, k_cache, v_cache})) return PA_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const int group = num_q_heads / num_kv_heads;
@@ -293,6 +302,7 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
     return PA_E_INVAL;
+  if (!rows_aligned16({out, q, k_cache, v_cache})) return PA_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (checks_enabled()) {
     std::vector<int32_t> cq, ck, bt;

@@ -587,19 +587,34 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   }
 
   const float l_tot = xor_sum<32>(l_run);
-  if (wave_active && my_row < Lq) {
+  if (wave_active) {
     const float inv = 1.f / l_tot;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
                    ((long)(q_start + my_row) * num_q_heads + h) * D;
-    // Item t of block db is head-dim element db*32 + 8*(t/4) + 4*lh + t%4.
+    // Item t of block db is head-dim element db*32 + 8*(t/4) + 4*lh + t%4:
+    // per 16 elements db*32 + 16*j .. + 15, the lane of half lh = 0 holds
+    // the quarters 0 and 2, its partner 32 lanes up the quarters 1 and 3.
+    // One lane swap per dword gives the lower lane the first 8 elements and
+    // its partner the last 8, so each stores 16 contiguous bytes.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        uint2 u;
-        u.x = pack_bf16x2(oacc[db][t4 * 4 + 0] * inv, oacc[db][t4 * 4 + 1] * inv);
-        u.y = pack_bf16x2(oacc[db][t4 * 4 + 2] * inv, oacc[db][t4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * t4 + 4 * lh) = u;
+      for (int j = 0; j < 2; ++j) {
+        unsigned w[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int t = (2 * j + q) * 4;
+          w[q][0] = pack_bf16x2(oacc[db][t + 0] * inv, oacc[db][t + 1] * inv);
+          w[q][1] = pack_bf16x2(oacc[db][t + 2] * inv, oacc[db][t + 3] * inv);
+        }
+        uint4 u;
+        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+        u.x = s0[0];
+        u.y = s1[0];
+        u.z = s0[1];
+        u.w = s1[1];
+        if (my_row < Lq) *reinterpret_cast<uint4*>(op + db * 32 + 16 * j + 8 * lh) = u;
       }
     }
   }

@@ -77,6 +77,8 @@ def test_decode_validation(lib):
     assert _decode(lib, maxl=1000, mb=64, ws=None) == pa.PA_E_WORKSPACE
     assert _decode(lib, maxl=1000, mb=64, ws=FAKE, wsb=16) == pa.PA_E_WORKSPACE
     assert _decode(lib, B=0) == pa.PA_OK                           # empty batch: no-op
+    for name in ("out", "q", "kc", "vc"):                          # 16-byte element rows
+        assert _decode(lib, **{name: ctypes.c_void_p(0x1008)}) == pa.PA_E_INVAL
 
 
 def _prefill(lib, **kw):
@@ -101,6 +103,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, B=0) == pa.PA_OK
     assert _prefill(lib, ws=FAKE, wsb=16) == pa.PA_E_WORKSPACE     # counter area too small
     assert _prefill(lib, ws=ctypes.c_void_p(0x1010), wsb=256) == pa.PA_E_INVAL   # unaligned
+    for name in ("out", "q", "kc", "vc"):                          # 16-byte element rows
+        assert _prefill(lib, **{name: ctypes.c_void_p(0x1008)}) == pa.PA_E_INVAL
     assert binding.PREFILL_WORKSPACE_BYTES == 256
 
 
