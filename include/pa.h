@@ -148,13 +148,16 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   max_seqlen_q, max_seqlen_k  host upper bounds of Lq and Lk
  *   head_dim      64 or 128
  *   workspace     NULL, or device memory of at least PA_PREFILL_WORKSPACE_BYTES
- *                 bytes, 256-byte aligned, holding a work counter that must be
- *                 zero before the first call that uses the memory (every call
- *                 leaves it zero).  With it, the query tiles left after each
- *                 workgroup's first go to whichever workgroup is free; without
- *                 it they are dealt in a fixed order.  Results are bitwise the
- *                 same either way.  Calls that run concurrently need
- *                 workspaces of their own.  PA_E_WORKSPACE if too small.
+ *                 bytes, 256-byte aligned, holding work counters: all of it
+ *                 must be zero before the first call that uses the memory
+ *                 (every call leaves it zero).  With it, the query tiles left
+ *                 after each workgroup's first go to whichever workgroup is
+ *                 free (within groups of workgroups that share an XCD, each
+ *                 group taking the tiles of its own KV heads, when the head
+ *                 count allows); without it they are dealt in a fixed order.
+ *                 Results are bitwise the same either way.  Calls that run
+ *                 concurrently need workspaces of their own.  PA_E_WORKSPACE
+ *                 if too small.
  * bf16 runs on the matrix cores; fp32 runs on the vector ALUs (and ignores
  * the workspace).
  * num_seqs == 0 or total_q == 0 is a no-op.

@@ -178,9 +178,9 @@ _prefill_ws = {}
 
 
 def prefill_workspace(device, stream=None):
-    """The zeroed work counter pa_prefill_varlen uses on (device, stream) when
-    the caller passes none: one per stream, since calls on one stream run in
-    order and each leaves the counter zero."""
+    """The zeroed work counters pa_prefill_varlen uses on (device, stream) when
+    the caller passes none: one set per stream, since calls on one stream run
+    in order and each leaves the counters zero."""
     torch = _torch()
     key = (torch.device(device).index or 0, _stream(stream) or 0)
     ws = _prefill_ws.get(key)

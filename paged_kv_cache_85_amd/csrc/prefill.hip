@@ -259,10 +259,28 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   ItemWalk walk{0, 0, 0};
   const int G = gridDim.x;
   const int gi = blockIdx.x;
+  // XCD groups.  The workgroups of a launch are placed on the chip's eight
+  // XCDs in turn (workgroup i on XCD i mod 8), and each XCD has an L2 of its
+  // own.  With a work counter and a KV-head/chunk count that is a multiple
+  // of 8, group x (the workgroups i = x mod 8) deals among itself only the
+  // items of head/chunk gh = x mod 8, heaviest first, through a counter of
+  // its own: the keys and values a head's query tiles re-read then come
+  // from one L2, and every group has the same work (heads cost the same).
+  // The item order and dealing within a group are those described above
+  // with G / 8 workgroups and inner / 8 head/chunks.
+  constexpr int kXcds = 8;
+  const bool grouped =
+      persistent && a.ticket != nullptr && inner % kXcds == 0 && G % kXcds == 0;
+  const int GX = grouped ? G / kXcds : G;          // workgroups dealing together
+  const int gx = grouped ? gi / kXcds : gi;        // this workgroup among them
+  const int xg = grouped ? gi % kXcds : 0;         // its group
+  const int innerx = grouped ? inner / kXcds : inner;
+  const int n_itemsx = grouped ? n_items / kXcds : n_items;
+  unsigned* const ticket = a.ticket != nullptr ? a.ticket + xg * 8 : nullptr;
   // Dynamic dealing needs every workgroup to hold a first item (each then
   // draws until a draw comes back past the end).
-  const bool dyn = persistent && a.ticket != nullptr && n_items > G;
-  const unsigned last_draw = (unsigned)(n_items - G) + (unsigned)G - 1u;
+  const bool dyn = persistent && ticket != nullptr && n_itemsx > GX;
+  const unsigned last_draw = (unsigned)(n_itemsx - GX) + (unsigned)GX - 1u;
   unsigned tk = 0;     // thread 0: the rank drawn during the current item
   bool drew = false;   // thread 0: whether that draw has been made
 
@@ -274,22 +292,23 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
       // The rank drawn during the previous item (drawn now if that item
       // ended before its draw point), published to the whole workgroup.
       if (tid == 0) {
-        if (!drew) tk = atomicAdd(a.ticket, 1u);
+        if (!drew) tk = atomicAdd(ticket, 1u);
         s_ticket = tk;
       }
       __syncthreads();
       const unsigned t = __builtin_amdgcn_readfirstlane(s_ticket);
       drew = false;
-      if ((long)G + t >= (long)n_items) {
+      if ((long)GX + t >= (long)n_itemsx) {
         if (t == last_draw && tid == 0)
-          __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      k = G + (int)t;
+      k = GX + (int)t;
     } else {
-      k = round * G + ((round & 1) ? G - 1 - gi : gi);
+      k = round * GX + ((round & 1) ? GX - 1 - gx : gx);
     }
-    if (!walk_to(walk, k, s_ntiles, num_seqs, n_qt, inner, lane, qt, b, gh)) break;
+    if (!walk_to(walk, k, s_ntiles, num_seqs, n_qt, innerx, lane, qt, b, gh)) break;
+    gh = gh * (grouped ? kXcds : 1) + xg;
   } else {
     if (round > 0) break;
     int x = gi;
@@ -517,7 +536,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     // the tile waits below then wait for one operation more than needed,
     // never fewer, since operations complete in issue order.)
     if (dyn && tid == 0 && kt == draw_kt) {
-      tk = atomicAdd(a.ticket, 1u);
+      tk = atomicAdd(ticket, 1u);
       drew = true;
     }
     if constexpr (DMA) {
