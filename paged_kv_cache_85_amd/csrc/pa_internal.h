@@ -71,6 +71,7 @@ struct PrefillArgs {
   float scale_log2;
   int persistent;   // set by the launcher: workgroups loop over work items
   unsigned* ticket; // work counter (null: every item dealt in a fixed order)
+  int xcd_groups;   // set by the launcher: deal each KV head's items within one XCD
 };
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);

@@ -261,16 +261,18 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   const int gi = blockIdx.x;
   // XCD groups.  The workgroups of a launch are placed on the chip's eight
   // XCDs in turn (workgroup i on XCD i mod 8), and each XCD has an L2 of its
-  // own.  With a work counter and a KV-head/chunk count that is a multiple
-  // of 8, group x (the workgroups i = x mod 8) deals among itself only the
-  // items of head/chunk gh = x mod 8, heaviest first, through a counter of
-  // its own: the keys and values a head's query tiles re-read then come
-  // from one L2, and every group has the same work (heads cost the same).
-  // The item order and dealing within a group are those described above
-  // with G / 8 workgroups and inner / 8 head/chunks.
+  // own.  When the launcher asks for it (sequences of several query tiles,
+  // which re-read their keys and values), with a work counter and a
+  // KV-head/chunk count that is a multiple of 8, group x (the workgroups
+  // i = x mod 8) deals among itself only the items of head/chunk
+  // gh = x mod 8, heaviest first, through a counter of its own: the keys and
+  // values a head's query tiles re-read then come from one L2, and every
+  // group has the same work (heads cost the same).  The item order and
+  // dealing within a group are those described above with G / 8 workgroups
+  // and inner / 8 head/chunks.
   constexpr int kXcds = 8;
-  const bool grouped =
-      persistent && a.ticket != nullptr && inner % kXcds == 0 && G % kXcds == 0;
+  const bool grouped = a.xcd_groups != 0 && persistent && a.ticket != nullptr &&
+                       inner % kXcds == 0 && G % kXcds == 0;
   const int GX = grouped ? G / kXcds : G;          // workgroups dealing together
   const int gx = grouped ? gi / kXcds : gi;        // this workgroup among them
   const int xg = grouped ? gi % kXcds : 0;         // its group
@@ -666,6 +668,13 @@ static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t str
   // (Tile counts are kept as 16-bit values: n_qt < 65536.)
   p.persistent = (a.num_seqs <= kMaxPersistSeqs && a.max_seqlen_q < (1 << 21) &&
                   n_items > cached_slots) ? 1 : 0;
+  // XCD groups pay off when the sequences average two query tiles or more
+  // (their later tiles re-read the keys and values of the earlier ones).
+  // Batches of mostly decode rows read every tile once, and there eight
+  // separate pools of items of unequal, unsorted cost only lengthen the tail
+  // (decode rows as one launch: 226 us grouped against 210 us).
+  constexpr int BMQ = 32 * (4 / HPW);
+  p.xcd_groups = (long long)a.total_q >= 2LL * BMQ * a.num_seqs ? 1 : 0;
   const long long grid = p.persistent ? cached_slots : n_items;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST, NT>), dim3((unsigned)grid), dim3(256),
                      0, stream, p, a.block_tables, a.cu_seqlens_q, a.cu_seqlens_k);
