@@ -278,6 +278,8 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   const int xg = grouped ? gi % kXcds : 0;         // its group
   const int innerx = grouped ? inner / kXcds : inner;
   const int n_itemsx = grouped ? n_items / kXcds : n_items;
+  // Group x's counter sits 32 bytes after group x - 1's: the eight fill the
+  // 256-byte workspace.
   unsigned* const ticket = a.ticket != nullptr ? a.ticket + xg * 8 : nullptr;
   // Dynamic dealing needs every workgroup to hold a first item (each then
   // draws until a draw comes back past the end).
