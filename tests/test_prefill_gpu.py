@@ -74,6 +74,40 @@ def test_prefill_work_counter_bitwise(config):
         assert int(ws.count_nonzero()) == 0, "the work counter must come back to zero"
 
 
+def test_prefill_many_sequences_deals_bitwise():
+    """150 sequences of two to five query tiles (8 KV heads, block 256): the
+    work-counter launch deals each KV head's tiles within one group of
+    workgroups and walks several 64-sequence chunks per group.  It must give
+    the fixed deal's bits and leave every counter at zero; sampled sequences
+    run alone match the oracle and their batched rows."""
+    import torch
+    spec = PrefillSpec("pre-many", 16, 8, 128, "bf16", 256, q_len_range=(130, 300),
+                       num_seqs=150, prefix_len=40)
+    case = make_prefill(spec, 84)
+    fixed, _, _ = run_prefill(case, workspace=False)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda:0")
+    for rep in range(2):
+        dealt, _, _ = run_prefill(case, workspace=ws)
+        assert np.array_equal(bits(dealt), bits(fixed)), f"call {rep}"
+        assert int(ws.count_nonzero()) == 0, "the work counters must come back to zero"
+    cq = case.cu_seqlens_q
+    for b in (0, 77, 149):
+        sub = prefill_subset(case, [b], perm_seed=b + 1)
+        alone = run_prefill(sub)[0]
+        assert np.array_equal(bits(alone), bits(fixed)[cq[b]:cq[b + 1]]), b
+        assert_close(f64(alone), _oracle(sub), "bf16", f"pre-many seq {b}")
+
+
+def test_prefill_beyond_persistent_batch():
+    """2100 one- to three-token prompts: more sequences than the persistent
+    launch keeps counts for, so one workgroup per item; against the oracle."""
+    spec = PrefillSpec("pre-2100", 4, 2, 64, "bf16", 16, q_len_range=(1, 3), num_seqs=2100,
+                       prefix_len=5)
+    case = make_prefill(spec, 85)
+    out, _, _ = run_prefill(case)
+    assert_close(f64(out), _oracle(case), "bf16", spec.name)
+
+
 def test_prefill_invariance_bitwise():
     spec = PrefillSpec("pre-inv", 16, 8, 128, "bf16", 16, q_len_range=(1, 1),
                        q_lens=(40, 130, 1, 77), prefix_lens=(0, 20, 256, 5))
