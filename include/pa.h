@@ -49,7 +49,10 @@
  *   - Outputs must not alias inputs; k/v must not alias the pools.
  *   - pa_decode and pa_prefill_varlen move element rows in 16-byte pieces:
  *     out, q and both pools must be 16-byte aligned (else PA_E_INVAL).
- *   - The library is stateless; calls on different streams may overlap.
+ *   - The library keeps no state between calls apart from a per-device cache
+ *     of each persistent kernel's occupancy, filled on first use (threads
+ *     that fill it together store the same value).  Calls on different
+ *     streams may overlap as long as each has a workspace of its own.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -94,9 +97,10 @@ int pa_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
 
 /*
  * Bytes of workspace pa_decode may need: a 256-byte work counter, then fp32
- * split-context partial results (running max, sum and unnormalised output
- * per sequence, query head and context partition).  Depends only on these
- * sizes.
+ * split-context partial results (unnormalised output, running max and sum
+ * per sequence, query head and 256-token context partition, for
+ * ceil(max_context_len / 256) partitions).  Depends only on these sizes.
+ * 0 when any size is <= 0.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len);
@@ -120,7 +124,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 once, e.g. with hipMemset); every call leaves it zero
  *                 again, so a workspace can be reused by any later call on
  *                 the same stream.  The rest is scratch.  Calls that run
- *                 concurrently need workspaces of their own.
+ *                 concurrently need workspaces of their own.  Only batches
+ *                 with a context longer than 256 tokens use it (else it
+ *                 may be NULL).  With PA_CHECK=1 a non-zero counter is
+ *                 rejected with PA_E_WORKSPACE.
  * num_seqs == 0 is a no-op.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -157,7 +164,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *                 count allows); without it they are dealt in a fixed order.
  *                 Results are bitwise the same either way.  Calls that run
  *                 concurrently need workspaces of their own.  PA_E_WORKSPACE
- *                 if too small.
+ *                 if too small, or (with PA_CHECK=1) if a counter is not
+ *                 zero.
  * bf16 runs on the matrix cores; fp32 runs on the vector ALUs (and ignores
  * the workspace).
  * num_seqs == 0 or total_q == 0 is a no-op.

@@ -17,7 +17,8 @@ PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
-EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_varlen",
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode",
+           "pa_prefill_varlen",
            "pa_qk_norm_rope_store", "pa_status_string", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append", "pa_bm_free", "pa_bm_block_table",
            "pa_bm_seq_info", "pa_bm_slots", "pa_bm_append_batch", "pa_bm_plan_decode",
@@ -118,6 +119,20 @@ def _stream(stream) -> Optional[int]:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _torch_stream(stream, device):
+    """The torch stream object the library will run on (for ordering the
+    binding's own allocations and fills on that same stream)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = int(getattr(stream, "cuda_stream", stream) or 0)
+    if handle == 0:
+        return torch.cuda.default_stream(device)
+    return torch.cuda.ExternalStream(handle, device=device)
+
+
 def _check(fn: str, rc: int) -> None:
     if rc != PA_OK:
         raise PAError(fn, rc)
@@ -151,7 +166,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     """q, out: [B, Hq, D]; block_tables: int32 [B, MB]; context_lens: int32 [B].
     workspace: a device tensor of at least pa_decode_workspace_bytes(...) bytes
     whose first 256 bytes were zeroed before its first use (every call leaves
-    them zero); allocated and zeroed here through torch when None."""
+    them zero); None: one kept per (device, stream) by decode_workspace()."""
     torch = _torch()
     dt = _dtype_code(q)
     B, hq, d = q.shape
@@ -161,8 +176,9 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, MB] and context_lens [B]")
     if workspace is None:
-        n = pa_decode_workspace_bytes(B, hq, d, max_context_len)
-        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(q.device, pa_decode_workspace_bytes(B, hq, d,
+                                                                          max_context_len),
+                                     stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().pa_decode(_ptr(out, "out", q.dtype), _ptr(q, "q"),
                          _ptr(k_cache, "k_cache", q.dtype), _ptr(v_cache, "v_cache", q.dtype),
@@ -175,6 +191,16 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
 
 PREFILL_WORKSPACE_BYTES = 256
 _prefill_ws = {}
+_decode_ws = {}
+
+
+def _zeroed_on(stream, device, nbytes: int):
+    """A zeroed uint8 device tensor allocated and filled on `stream`, so that
+    the fill is ordered before the library's kernels on that stream and the
+    caching allocator only reuses the memory in that stream's order."""
+    torch = _torch()
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def prefill_workspace(device, stream=None):
@@ -185,8 +211,22 @@ def prefill_workspace(device, stream=None):
     key = (torch.device(device).index or 0, _stream(stream) or 0)
     ws = _prefill_ws.get(key)
     if ws is None:
-        ws = torch.zeros(PREFILL_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+        ws = _zeroed_on(stream, device, PREFILL_WORKSPACE_BYTES)
         _prefill_ws[key] = ws
+    return ws
+
+
+def decode_workspace(device, nbytes: int, stream=None):
+    """A decode workspace of at least nbytes for (device, stream), zeroed on
+    that stream when it is made; kept and reused by later calls on the same
+    stream (each call leaves its counter zero), replaced by a larger one when
+    a call needs more."""
+    torch = _torch()
+    key = (torch.device(device).index or 0, _stream(stream) or 0)
+    ws = _decode_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = _zeroed_on(stream, device, nbytes)
+        _decode_ws[key] = ws
     return ws
 
 

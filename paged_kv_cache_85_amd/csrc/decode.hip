@@ -966,22 +966,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
 
 template <typename E, int D, int HG>
 static int launch_persistent(const RowAttnArgs& a, hipStream_t stream) {
-  // One wave per resident slot: CUs x the kernel's occupancy, queried once
-  // per device.
-  static int cached_device = -1, cached_waves = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (dev != cached_device) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(decode_persistent_kernel<E, D, HG>), 64, 0) !=
-        hipSuccess)
-      return -1;
-    cached_waves = max(1, cus * max(per_cu, 1));
-    cached_device = dev;
-  }
+  // One wave per resident slot: CUs x the kernel's occupancy.
+  static std::atomic<int> slots_cache[kMaxDevices];
+  const int cached_waves = resident_blocks(
+      reinterpret_cast<const void*>(decode_persistent_kernel<E, D, HG>), 64, slots_cache);
+  if (cached_waves < 0) return -1;
   const long long max_items =
       (long long)a.num_rows * a.num_kv_heads * a.head_chunks * a.max_parts;
   const int waves = (int)min((long long)cached_waves, max_items);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -103,6 +105,31 @@ constexpr float kNegBig = -1.0e30f;
 
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
   return min(max(blk, 0), num_blocks - 1);
+}
+
+// Persistent launches size their grid as CUs x resident blocks per CU of the
+// kernel, queried once per device and kept in `cache` (one table per kernel;
+// zero means not known yet).  Host threads that ask for the first time
+// together may each query the runtime; they store the same value, so the
+// table needs no lock.  Devices past kMaxDevices are queried on every call.
+constexpr int kMaxDevices = 64;
+
+inline int resident_blocks(const void* kernel, int threads, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return -1;
+  const int v = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 }  // namespace pa

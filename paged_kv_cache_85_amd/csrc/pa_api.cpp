@@ -169,29 +169,37 @@ int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void*
   return launch_status();
 }
 
+}  // extern "C"
+
 // The decode workspace starts with the persistent kernel's work counter, at
-// a fixed place whatever the sizes of the call.
+// a fixed place whatever the sizes of the call, then the split-context
+// partials of kDecodePartition-token partitions:
+// [work counter: 256 B][partial outputs][partial max / sum].
 constexpr size_t kCounterBytes = 256;
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const size_t parts = ((size_t)max_context_len + pa::kMinPartition - 1) / pa::kMinPartition;
+struct DecodeLayout {
+  int max_parts;   // partitions of the longest context
+  size_t ml_off;   // byte offset of the (max, sum) pairs
+  size_t total;    // bytes
+};
+
+static DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len) {
+  DecodeLayout l{};
+  l.max_parts = (int)(((long long)max_context_len + pa::kDecodePartition - 1) /
+                      pa::kDecodePartition);
   const size_t heads = (size_t)num_seqs * num_q_heads;
-  // [work counter: 256 B][partial outputs][partial max / sum]
-  const size_t o_bytes = heads * parts * head_dim * sizeof(float);
-  const size_t ml_off = (kCounterBytes + o_bytes + 255) & ~(size_t)255;
-  return ml_off + heads * parts * 2 * sizeof(float);
+  const size_t o_bytes = heads * (size_t)l.max_parts * head_dim * sizeof(float);
+  l.ml_off = (kCounterBytes + o_bytes + 255) & ~(size_t)255;
+  l.total = l.ml_off + heads * (size_t)l.max_parts * 2 * sizeof(float);
+  return l;
 }
 
-// Tokens per context partition (four waves of 64 tokens).  It is fixed, not
-// tuned to the batch, so a row's arithmetic depends only on its own tokens:
-// the output is bitwise the same whether a sequence runs alone or batched,
-// whatever its physical block IDs or the block size.
-#ifndef PA_DECODE_PARTITION
-#define PA_DECODE_PARTITION 256
-#endif
-constexpr int kPartitionTokens = PA_DECODE_PARTITION;
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  return decode_layout(num_seqs, num_q_heads, head_dim, max_context_len).total;
+}
 
 static int heads_per_wg(int group, int head_dim) {
   const int cap = head_dim == 64 ? 8 : 4;
@@ -200,12 +208,24 @@ static int heads_per_wg(int group, int head_dim) {
   return 1;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
-              float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
-              void* stream) {
+// Work counters must be zero when a call starts (each call leaves them so).
+// Under PA_CHECK the first `n` 32-byte-spaced counters are read back.
+static int counters_zero(const void* workspace, int n, hipStream_t s) {
+  std::vector<int32_t> c;
+  if (!fetch(c, static_cast<const int32_t*>(workspace), (long long)n * 8, s)) return PA_E_HIP;
+  for (int i = 0; i < n; ++i)
+    if (c[(size_t)i * 8] != 0) return PA_E_WORKSPACE;
+  return PA_OK;
+}
+
+namespace pa {
+
+int decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, float scale, int32_t dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t s) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
       block_size < 1 || max_blocks_per_seq < 1 || max_context_len < 1 || !isfinite(scale) ||
       !(scale > 0.f))
@@ -218,16 +238,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_E_INVAL;
   if (!rows_aligned16({out, q, k_cache, v_cache})) return PA_E_INVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   const int group = num_q_heads / num_kv_heads;
   const int hg = heads_per_wg(group, head_dim);
-  const int part = kPartitionTokens;
-  const int max_parts = (max_context_len + part - 1) / part;
-  if (max_parts > 1) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                  max_context_len);
-    if (!workspace || workspace_bytes < need) return PA_E_WORKSPACE;
+  const DecodeLayout lay = decode_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  if (lay.max_parts > 1) {
+    if (!workspace || workspace_bytes < lay.total) return PA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_E_INVAL;
   }
   if (checks_enabled()) {
@@ -239,6 +255,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
       if (!blocks_ok(bt, b, max_blocks_per_seq, lens[b], block_size, num_blocks))
         return PA_E_INVAL;
     }
+    if (lay.max_parts > 1) {
+      const int rc = counters_zero(workspace, 1, s);
+      if (rc != PA_OK) return rc;
+    }
   }
 
   pa::RowAttnArgs a{};
@@ -248,15 +268,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  if (max_parts > 1) {
-    const size_t parts_bound =
-        ((size_t)max_context_len + pa::kMinPartition - 1) / pa::kMinPartition;
-    const size_t heads = (size_t)num_seqs * num_q_heads;
-    const size_t o_bytes = heads * parts_bound * head_dim * sizeof(float);
-    const size_t ml_off = (kCounterBytes + o_bytes + 255) & ~(size_t)255;
+  if (lay.max_parts > 1) {
     a.ticket = static_cast<unsigned*>(workspace);
     a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
   }
   a.num_rows = num_seqs;
   a.num_seqs = num_seqs;
@@ -270,11 +285,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.block_size = block_size;
   a.block_size_log2 = log2_exact(block_size);
   a.max_context = max_context_len;
-  a.part_tokens = part;
-  a.max_parts = max_parts;
+  a.part_tokens = pa::kDecodePartition;
+  a.max_parts = lay.max_parts;
   a.scale_log2 = (float)((double)scale * kLog2e);
   if (pa::launch_decode(a, head_dim, dtype, s)) return PA_E_UNSUPPORTED;
   return launch_status();
+}
+
+size_t decode_scratch_need(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                           int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const DecodeLayout l = decode_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  return l.max_parts > 1 ? l.total : 0;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+              float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return pa::decode_entry(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq, max_context_len, scale, dtype, workspace,
+                          workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -314,6 +352,10 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
       const int lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
       if (lq < 0 || lk < lq || lq > max_seqlen_q || lk > max_seqlen_k) return PA_E_INVAL;
       if (!blocks_ok(bt, b, max_blocks_per_seq, lk, block_size, num_blocks)) return PA_E_INVAL;
+    }
+    if (workspace && dtype == PA_DTYPE_BF16) {
+      const int rc = counters_zero(workspace, 8, s);
+      if (rc != PA_OK) return rc;
     }
   }
   const int group = num_q_heads / num_kv_heads;

@@ -6,9 +6,27 @@
 
 namespace pa {
 
-// Tokens per split-context partition are a multiple of this; the workspace
-// bound assumes the smallest partition.
-constexpr int kMinPartition = 64;
+// Tokens per decode context partition (four waves of 64 tokens).  It is
+// fixed, not tuned to the batch, so a row's arithmetic depends only on its
+// own tokens: the output is bitwise the same whether a sequence runs alone
+// or batched, whatever its physical block IDs or the block size.
+#ifndef PA_DECODE_PARTITION
+#define PA_DECODE_PARTITION 256
+#endif
+constexpr int kDecodePartition = PA_DECODE_PARTITION;
+
+// pa_decode after its stream argument is converted (shared by the entry
+// points that differ only in where the workspace comes from).
+int decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, float scale, int32_t dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+// Workspace bytes decode_entry needs for these sizes (0: none).
+size_t decode_scratch_need(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                           int32_t max_context_len);
 
 int launch_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
                     const int32_t* slot_mapping, int num_tokens, long long row_bytes,

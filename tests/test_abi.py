@@ -145,3 +145,12 @@ def test_prologue_validation(lib):
     assert _prologue(lib, q=ctypes.c_void_p(0x1008)) == pa.PA_E_INVAL   # not 16-byte aligned
     assert _prologue(lib, T=-1) == pa.PA_E_INVAL
     assert _prologue(lib, T=0, q=None) == pa.PA_OK
+
+
+def test_decode_workspace_sized_for_its_partitions(lib):
+    # [256 B counter][B*Hq*parts*D fp32, 256-aligned][B*Hq*parts*2 fp32], parts = ceil(L / 256)
+    B, hq, d, L = 256, 16, 128, 2048
+    parts = -(-L // 256)
+    o = B * hq * parts * d * 4
+    ml_off = (256 + o + 255) // 256 * 256
+    assert pa.pa_decode_workspace_bytes(B, hq, d, L) == ml_off + B * hq * parts * 2 * 4
