@@ -137,6 +137,33 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments and results are those of pa_decode
+ * (same kernels, same bits).  The split-context workspace is a device array
+ * inside the library, PA_NOALLOC_SCRATCH_BYTES bytes per GPU, created when
+ * the library is loaded on that GPU and held until the process ends; the
+ * call allocates nothing.  Its work counter is cleared on `stream` by a small
+ * kernel (no memset node) before each call that uses it.
+ *   Limit: pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *   max_context_len) must not exceed PA_NOALLOC_SCRATCH_BYTES, else
+ *   PA_E_WORKSPACE (nothing enqueued).  Batches whose contexts fit one
+ *   256-token partition use no workspace and have no limit.
+ *   Every call on a GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (different streams, or several host threads) race and give
+ *   undefined results; serialise them, or use pa_decode with a workspace
+ *   per stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      int32_t dtype, void* stream);
+
 /* Workspace bytes pa_prefill_varlen takes (its work counter). */
 #define PA_PREFILL_WORKSPACE_BYTES 256
 

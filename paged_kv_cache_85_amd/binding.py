@@ -17,7 +17,7 @@ PA_DTYPE_F32, PA_DTYPE_BF16 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
-EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode",
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_noalloc",
            "pa_prefill_varlen",
            "pa_qk_norm_rope_store", "pa_status_string", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append", "pa_bm_free", "pa_bm_block_table",
@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                 f32, i32, vp, sz, vp]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, i32, f32, i32, vp]
+        L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, i32, i32, i32, f32, i32, vp, sz, vp]
         L.pa_prefill_varlen.restype = ctypes.c_int
@@ -189,7 +192,30 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     _check("pa_decode", rc)
 
 
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                      max_context_len: int, scale: float, stream=None) -> None:
+    """pa_decode with the library's own per-GPU scratch array as its workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    B, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    rc = lib().pa_decode_noalloc(_ptr(out, "out", q.dtype), _ptr(q, "q"),
+                                 _ptr(k_cache, "k_cache", q.dtype),
+                                 _ptr(v_cache, "v_cache", q.dtype),
+                                 _ptr(block_tables, "block_tables", torch.int32),
+                                 _ptr(context_lens, "context_lens", torch.int32), B, hq, hkv, d,
+                                 nb, bs, block_tables.shape[1], int(max_context_len),
+                                 float(scale), dt, _stream(stream))
+    _check("pa_decode_noalloc", rc)
+
+
 PREFILL_WORKSPACE_BYTES = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 _prefill_ws = {}
 _decode_ws = {}
 

@@ -147,6 +147,27 @@ def test_prologue_validation(lib):
     assert _prologue(lib, T=0, q=None) == pa.PA_OK
 
 
+def test_decode_noalloc_validation(lib):
+    f = lib.pa_decode_noalloc
+
+    def call(B=4, hq=16, hkv=8, d=128, nb=64, bs=16, mb=8, maxl=128, out=FAKE):
+        return f(out, FAKE, FAKE, FAKE, FAKE, FAKE, B, hq, hkv, d, nb, bs, mb, maxl, 0.125, 1,
+                 None)
+
+    # a batch whose partials exceed the library's scratch array: refused
+    # before any device call
+    big = pa.pa_decode_workspace_bytes(4096, 64, 128, 8192)
+    assert big > binding.NOALLOC_SCRATCH_BYTES
+    assert call(B=4096, hq=64, hkv=8, mb=512, maxl=8192) == pa.PA_E_WORKSPACE
+    # one-partition contexts need no scratch: the argument checks answer
+    assert call(hq=12, hkv=8) == pa.PA_E_INVAL
+    assert call(d=96) == pa.PA_E_UNSUPPORTED
+    assert call(out=None) == pa.PA_E_INVAL
+    assert call(B=0) == pa.PA_OK
+    # the Qwen3-shaped decode batch fits the scratch array
+    assert pa.pa_decode_workspace_bytes(256, 16, 128, 2048) <= binding.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_workspace_sized_for_its_partitions(lib):
     # [256 B counter][B*Hq*parts*D fp32, 256-aligned][B*Hq*parts*2 fp32], parts = ceil(L / 256)
     B, hq, d, L = 256, 16, 128, 2048
