@@ -647,363 +647,6 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   }
 }
 
-// ---------------------------------------------------------------- two heads per wave
-//
-// Query groups of even size (Qwen3: 16 query heads over 8 KV heads) run this
-// form.  A wave owns 32 query rows of TWO query heads of the same KV head, so
-// every K operand read from LDS feeds two score products (one per head) and
-// every transposed V operand read feeds two PV products: half the LDS operand
-// reads per matrix instruction of the one-head form above.  A workgroup is
-// WPG such waves, one below the other (BMQ = 32 * WPG rows of the same two
-// heads), and it shares each key/value tile among them.  The register file
-// holds both heads' accumulators (one wave per SIMD).
-//
-// Each head's arithmetic is, instruction for instruction, that of the
-// one-head kernel: the same 32-row groups, the same chained score products,
-// mask, row max, lazy rescale decision (taken over the wave's 32 rows of that
-// head), exponentials, rounding of P, and PV accumulation order.  The two
-// forms therefore give the same bits, whichever one a launch takes.
-template <int D, int WPG, int NST, bool NT>
-__global__ __launch_bounds__(64 * WPG, 1) void prefill_pair_kernel(
-    PrefillArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k) {
-  constexpr int BN = 32;
-  constexpr int NTH = 64 * WPG;
-  constexpr int BMQ = 32 * WPG;
-  constexpr int KC = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int NI = BN * CPR / NTH;         // loads per thread per tensor per tile
-  static_assert(NI >= 1 && NI * NTH == BN * CPR, "tile split");
-  static_assert(NST >= 2 && NST <= 4, "stage count");
-
-  __shared__ __attribute__((aligned(16))) uint16_t st[NST][2 * BN * D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-
-  const int num_seqs = a.num_seqs;
-  const int hchunks = a.group / 2;           // head pairs per KV head
-  const int inner = a.num_kv_heads * hchunks;
-  const int n_qt = (a.max_seqlen_q + BMQ - 1) / BMQ;
-
-  // Items and their deal: as in the one-head kernel, with head pairs in
-  // place of head chunks.
-  __shared__ uint16_t s_ntiles[kMaxPersistSeqs];
-  __shared__ int s_items[WPG];
-  __shared__ unsigned s_ticket;
-  const bool persistent = a.persistent != 0;
-  int n_items = 0;
-  if (persistent) {
-    int mine = 0;
-    for (int i = tid; i < num_seqs; i += NTH) {
-      const int qs = cu_q[i], qe = cu_q[i + 1], kl = cu_k[i + 1] - cu_k[i];
-      int nq = 0;
-      if (qs >= 0 && qs < a.total_q) {
-        const int lk = min(min(kl, a.max_seqlen_k), a.max_blocks_per_seq * a.block_size);
-        const int lq = min(min(min(qe - qs, a.max_seqlen_q), lk), a.total_q - qs);
-        nq = lq > 0 ? (lq + BMQ - 1) / BMQ : 0;
-      }
-      s_ntiles[i] = (uint16_t)nq;
-      mine += nq;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
-    if (lane == 0) s_items[w] = mine;
-    __syncthreads();
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < WPG; ++i) tot += s_items[i];
-    n_items = tot * inner;
-  }
-  ItemWalk walk{0, 0, 0};
-  const int G = gridDim.x;
-  const int gi = blockIdx.x;
-  constexpr int kXcds = 8;
-  const bool grouped = a.xcd_groups != 0 && persistent && a.ticket != nullptr &&
-                       inner % kXcds == 0 && G % kXcds == 0;
-  const int GX = grouped ? G / kXcds : G;
-  const int gx = grouped ? gi / kXcds : gi;
-  const int xg = grouped ? gi % kXcds : 0;
-  const int innerx = grouped ? inner / kXcds : inner;
-  const int n_itemsx = grouped ? n_items / kXcds : n_items;
-  unsigned* const ticket = a.ticket != nullptr ? a.ticket + xg * 8 : nullptr;
-  const bool dyn = persistent && ticket != nullptr && n_itemsx > GX;
-  const unsigned last_draw = (unsigned)(n_itemsx - GX) + (unsigned)GX - 1u;
-  unsigned tk = 0;
-  bool drew = false;
-
-  for (int round = 0;; ++round) {
-  int qt, b, gh;
-  if (persistent) {
-    int k;
-    if (dyn && round > 0) {
-      if (tid == 0) {
-        if (!drew) tk = atomicAdd(ticket, 1u);
-        s_ticket = tk;
-      }
-      __syncthreads();
-      const unsigned t = __builtin_amdgcn_readfirstlane(s_ticket);
-      drew = false;
-      if ((long)GX + t >= (long)n_itemsx) {
-        if (t == last_draw && tid == 0)
-          __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      k = GX + (int)t;
-    } else {
-      k = round * GX + ((round & 1) ? GX - 1 - gx : gx);
-    }
-    if (!walk_to(walk, k, s_ntiles, num_seqs, n_qt, innerx, lane, qt, b, gh)) break;
-    gh = gh * (grouped ? kXcds : 1) + xg;
-  } else {
-    if (round > 0) break;
-    int x = gi;
-    gh = x % inner;
-    x /= inner;
-    b = x % num_seqs;
-    qt = n_qt - 1 - x / num_seqs;
-  }
-  const int g = gh / hchunks;
-  const int hc = gh % hchunks;
-
-  const int q_start = __builtin_amdgcn_readfirstlane(cu_q[b]);
-  const int q_end = __builtin_amdgcn_readfirstlane(cu_q[b + 1]);
-  const int k_len = __builtin_amdgcn_readfirstlane(cu_k[b + 1] - cu_k[b]);
-  if (q_start < 0 || q_start >= a.total_q) continue;
-  const int Lk = min(min(k_len, a.max_seqlen_k), a.max_blocks_per_seq * a.block_size);
-  const int Lq = min(min(min(q_end - q_start, a.max_seqlen_q), Lk), a.total_q - q_start);
-  if (qt < 0 || qt * BMQ >= Lq) continue;
-  const int delta = Lk - Lq;
-  const float scale_log2 = a.scale_log2;
-  const int num_q_heads = a.num_q_heads;
-
-  const int h0 = g * a.group + hc * 2;       // this wave's heads: h0, h0 + 1
-  const int row0 = qt * BMQ + w * 32;
-  const bool wave_active = row0 < Lq;
-  const int kmax_wave = delta + min(row0 + 32, Lq) - 1;
-  const int kmax_wg = delta + min(qt * BMQ + BMQ, Lq) - 1;
-  const int n_tiles = kmax_wg / BN + 1;
-  const int draw_kt = max(0, n_tiles - 3);
-
-  bf16x8 qB[2][KC];
-  const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
-  const int32_t* bt = tables + (long)b * a.max_blocks_per_seq;
-  const int slot_elems = a.num_kv_heads * D;
-  const unsigned row_bytes = (unsigned)slot_elems * 2u;
-  const int bs = a.block_size;
-  const int bs_log2 = a.block_size_log2;
-  const int nblk = a.num_blocks;
-
-  unsigned src_off[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int s = (w * NI + i) * 64 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ tile_swz<D>(r);
-    src_off[i] = (unsigned)r * row_bytes + (unsigned)(c * 16);
-  }
-
-  auto request = [&](uint16_t* dk, uint16_t* dv, int kt, int blk_id) __attribute__((always_inline)) {
-    const int t0 = kt * BN;
-    const int blk = clamp_block(blk_id, nblk);
-    const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
-    const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
-    const u32x4 rk = stream_rsrc(kcache + base, bytes);
-    const u32x4 rv = stream_rsrc(vcache + base, bytes);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16<NT>(rk, dk + (w * NI + i) * 512, src_off[i]);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16<NT>(rv, dv + (w * NI + i) * 512, src_off[i]);
-  };
-
-  f32x16 oacc[2][DB];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[hh][db] = f32x16{};
-  float m_run[2] = {kNegBig, kNegBig};
-  float l_run[2] = {0.f, 0.f};
-  const int my_row = row0 + lr;
-  const int klim = delta + my_row;
-  const int krow = swap_bits_2_3(lr);
-  const int kswz = tile_swz<D>(krow);
-  const int tr_j = lane & 15;
-  const int tr_key = 8 * lh + tr_j / 4;
-  const int tr_el = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
-
-  auto compute = [&](const uint16_t* sk, const uint16_t* sv, int kt) __attribute__((always_inline)) {
-    // Scores of both heads from one K operand read per 16-wide slice.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      const int pc = (2 * kk + lh) ^ kswz;
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(sk + krow * D + pc * 8);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qB[0][kk], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qB[1][kk], sacc[1], 0, 0, 0);
-    }
-    // Item t holds the raw score of key kt*BN + 16*(t/8) + 8*lh + t%8.
-    const bool need_mask = (kt * BN + BN - 1 > delta + row0) || (kt * BN + BN > Lk);
-    if (need_mask) {
-      const int thr = min(klim, Lk - 1) - (kt * BN + 8 * lh);
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (16 * (t >> 3) + (t & 7) > thr) {
-          sacc[0][t] = -INFINITY;
-          sacc[1][t] = -INFINITY;
-        }
-    }
-    bf16x8 pB[2][2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float mx = sacc[hh][0];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, sacc[hh][t]);
-      mx = xor_max<32>(mx) * scale_log2;
-      if (__any(mx > m_run[hh] + 8.f)) {
-        const float mn = fmaxf(m_run[hh], mx);
-        const float alpha = fast_exp2(m_run[hh] - mn);
-        m_run[hh] = mn;
-        l_run[hh] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) oacc[hh][db][t] *= alpha;
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pr = fast_exp2(fmaf(sacc[hh][kc * 8 + e], scale_log2, -m_run[hh]));
-          psum += pr;
-          pB[hh][kc][e] = (__bf16)pr;
-        }
-      }
-      l_run[hh] += psum;
-    }
-    // PV of both heads from one transposed V operand per (key slice, D slice).
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x4 part[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key = kc * 16 + tr_key + 4 * half;
-          const int el = db * 32 + tr_el;
-          const int pc = (el >> 3) ^ tile_swz<D>(key);
-          part[half] = lds_read_tr(sv + key * D + pc * 8 + (el & 7));
-        }
-        const bf16x8 A = {part[0][0], part[0][1], part[0][2], part[0][3],
-                          part[1][0], part[1][1], part[1][2], part[1][3]};
-        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pB[0][kc], oacc[0][db], 0, 0, 0);
-        oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pB[1][kc], oacc[1][db], 0, 0, 0);
-      }
-    }
-  };
-
-  int blk_next = 0;
-  if (NST - 1 < n_tiles) blk_next = bt[((NST - 1) * BN) >> bs_log2];
-
-  auto step = [&](auto stage, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage)::value;
-    uint16_t* sk = st[S];
-    uint16_t* nk = st[(S + NST - 1) % NST];
-    uint16_t* sv = sk + BN * D;
-    uint16_t* nv = nk + BN * D;
-    if (dyn && tid == 0 && kt == draw_kt) {
-      tk = atomicAdd(ticket, 1u);
-      drew = true;
-    }
-    wait_tiles<2 * NI, NST - 2>(min(NST - 2, n_tiles - 1 - kt));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NST - 1 < n_tiles) {
-      request(nk, nv, kt + NST - 1, blk_next);
-      if (kt + NST < n_tiles) blk_next = bt[((kt + NST) * BN) >> bs_log2];
-    }
-    if (wave_active && kt * BN <= kmax_wave) compute(sk, sv, kt);
-  };
-
-#pragma unroll
-  for (int t = 0; t < NST - 1; ++t)
-    if (t < n_tiles) request(st[t], st[t] + BN * D, t, bt[(t * BN) >> bs_log2]);
-  {
-    if (wave_active && my_row < Lq) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((long)(q_start + my_row) * num_q_heads + h0) * D + lh * 8;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk)
-          qB[hh][kk] = *reinterpret_cast<const bf16x8*>(qp + hh * D + kk * 16);
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) qB[hh][kk] = bf16x8{};
-    }
-  }
-  vm_wait<0>();
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  for (int kt = 0; kt < n_tiles; kt += NST) {
-    step(I0{}, kt);
-    if (kt + 1 >= n_tiles) break;
-    step(I1{}, kt + 1);
-    if constexpr (NST > 2) {
-      if (kt + 2 >= n_tiles) break;
-      step(I2{}, kt + 2);
-    }
-    if constexpr (NST > 3) {
-      if (kt + 3 >= n_tiles) break;
-      step(I3{}, kt + 3);
-    }
-  }
-
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const float l_tot = xor_sum<32>(l_run[hh]);
-    if (wave_active) {
-      const float inv = 1.f / l_tot;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
-                     ((long)(q_start + my_row) * num_q_heads + h0 + hh) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          unsigned wv[2][2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int t = (2 * j + q) * 4;
-            wv[q][0] = pack_bf16x2(oacc[hh][db][t + 0] * inv, oacc[hh][db][t + 1] * inv);
-            wv[q][1] = pack_bf16x2(oacc[hh][db][t + 2] * inv, oacc[hh][db][t + 3] * inv);
-          }
-          uint4 u;
-          const auto s0 = __builtin_amdgcn_permlane32_swap(wv[0][0], wv[1][0], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(wv[0][1], wv[1][1], false, false);
-          u.x = s0[0];
-          u.y = s1[0];
-          u.z = s0[1];
-          u.w = s1[1];
-          if (my_row < Lq) *reinterpret_cast<uint4*>(op + db * 32 + 16 * j + 8 * lh) = u;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  }
-}
-
 // Persistent launches keep one 16-bit query-tile count per sequence in LDS:
 // at most kMaxPersistSeqs sequences, each of at most 0xffff query tiles.
 static bool persistent_ok(const PrefillArgs& a, long long n_items, int slots, int bmq) {
@@ -1039,40 +682,6 @@ static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t str
   return 0;
 }
 
-#ifndef PA_PREFILL_PAIR
-#define PA_PREFILL_PAIR 0
-#endif
-#ifndef PA_PAIR_WPG
-#define PA_PAIR_WPG 2
-#endif
-#ifndef PA_PAIR_NST
-#define PA_PAIR_NST 3
-#endif
-
-template <int D, bool NT>
-static int launch_pair(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int WPG = PA_PAIR_WPG;
-  constexpr int NST = PA_PAIR_NST;
-  constexpr int BMQ = 32 * WPG;
-  const long long n_qt = (a.max_seqlen_q + BMQ - 1) / BMQ;
-  const long long n_items = n_qt * a.num_seqs * (long long)a.num_kv_heads * (a.group / 2);
-  if (n_items <= 0) return 0;
-  if (n_items > 0x7fffffffLL) return -1;
-  static std::atomic<int> slots_cache[kMaxDevices];
-  const int slots = resident_blocks(
-      reinterpret_cast<const void*>(prefill_pair_kernel<D, WPG, NST, NT>), 64 * WPG,
-      slots_cache);
-  if (slots < 0) return -1;
-  PrefillArgs p = a;
-  p.persistent = persistent_ok(a, n_items, slots, BMQ) ? 1 : 0;
-  p.xcd_groups = xcd_groups_ok(a, BMQ) ? 1 : 0;
-  const long long grid = p.persistent ? slots : n_items;
-  hipLaunchKernelGGL((prefill_pair_kernel<D, WPG, NST, NT>), dim3((unsigned)grid),
-                     dim3(64 * WPG), 0, stream, p, a.block_tables, a.cu_seqlens_q,
-                     a.cu_seqlens_k);
-  return 0;
-}
-
 template <int D, int HPW>
 static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BMQ = 32 * (4 / HPW);
@@ -1086,13 +695,7 @@ static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
     // row per sequence), each key/value tile is read by a single item:
     // those launches stream the tiles past the caches, as decode does; any
     // longer query tile re-reads its sequence's tiles through L2.
-    const bool nt = a.max_seqlen_q == 1;
-    // Query groups of even size: two heads per wave.
-    if constexpr (D == 128) {
-      if (PA_PREFILL_PAIR && a.group % 2 == 0 && PA_PREFILL_BN == 32)
-        return nt ? launch_pair<D, true>(a, stream) : launch_pair<D, false>(a, stream);
-    }
-    if (nt) return launch_items<D, HPW, true, true>(a, n_items, stream);
+    if (a.max_seqlen_q == 1) return launch_items<D, HPW, true, true>(a, n_items, stream);
     return launch_items<D, HPW, true, false>(a, n_items, stream);
   }
   return launch_items<D, HPW, false, false>(a, n_items, stream);
