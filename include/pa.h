@@ -95,11 +95,15 @@ int pa_store_kv(const void* k, const void* v, void* k_cache, void* v_cache,
                 int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
                 void* stream);
 
+/* Tokens per split-context partition of pa_decode (fixed, so that a row's
+ * result depends only on its own tokens). */
+#define PA_DECODE_PARTITION_TOKENS 512
+
 /*
  * Bytes of workspace pa_decode may need: a 256-byte work counter, then fp32
  * split-context partial results (unnormalised output, running max and sum
- * per sequence, query head and 256-token context partition, for
- * ceil(max_context_len / 256) partitions).  Depends only on these sizes.
+ * per sequence, query head and 512-token context partition, for
+ * ceil(max_context_len / 512) partitions).  Depends only on these sizes.
  * 0 when any size is <= 0.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -125,7 +129,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 again, so a workspace can be reused by any later call on
  *                 the same stream.  The rest is scratch.  Calls that run
  *                 concurrently need workspaces of their own.  Only batches
- *                 with a context longer than 256 tokens use it (else it
+ *                 with a context longer than 512 tokens use it (else it
  *                 may be NULL).  With PA_CHECK=1 a non-zero counter is
  *                 rejected with PA_E_WORKSPACE.
  * num_seqs == 0 is a no-op.
@@ -149,7 +153,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   Limit: pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
  *   max_context_len) must not exceed PA_NOALLOC_SCRATCH_BYTES, else
  *   PA_E_WORKSPACE (nothing enqueued).  Batches whose contexts fit one
- *   256-token partition use no workspace and have no limit.
+ *   512-token partition use no workspace and have no limit.
  *   Every call on a GPU shares that GPU's array: calls that may overlap on
  *   one GPU (different streams, or several host threads) race and give
  *   undefined results; serialise them, or use pa_decode with a workspace

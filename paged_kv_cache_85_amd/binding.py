@@ -215,6 +215,7 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
 
 
 PREFILL_WORKSPACE_BYTES = 256
+DECODE_PARTITION_TOKENS = 512      # PA_DECODE_PARTITION_TOKENS
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 _prefill_ws = {}
 _decode_ws = {}

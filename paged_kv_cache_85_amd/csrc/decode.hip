@@ -8,7 +8,7 @@
 // bf16 KV at a query group of 2), so the kernels are organised around the
 // memory stream, not the matrix cores:
 //
-//  * the unit of work is an item = (sequence, 256-token context partition,
+//  * the unit of work is an item = (sequence, 512-token context partition,
 //    KV head); the query heads of the KV head's group (up to HG of them)
 //    share every K/V row loaded, so each KV byte is read once per group;
 //  * one wave folds an item in stages of SUB tokens; each lane loads 16
@@ -317,7 +317,9 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   const int nb = a.num_blocks;
 
   constexpr bool kLdsTable = !BIG && !VARLEN;
-  constexpr int kMaxTable = kLdsTable ? 256 : 1;  // blocks of one 256-token partition
+  // Blocks of one decode partition: at most its token count (block size 1).
+  constexpr int kMaxTable = kLdsTable ? kDecodePartition : 1;
+  static_assert(!kLdsTable || kDecodePartition % 64 == 0, "partition size");
   __shared__ int s_bt[kMaxTable];
   int first_blk = 0;
   if constexpr (kLdsTable) {

@@ -4,14 +4,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pa.h"
+
 namespace pa {
 
-// Tokens per decode context partition (four waves of 64 tokens).  It is
-// fixed, not tuned to the batch, so a row's arithmetic depends only on its
-// own tokens: the output is bitwise the same whether a sequence runs alone
-// or batched, whatever its physical block IDs or the block size.
+// Tokens per decode context partition.  It is fixed, not tuned to the
+// batch, so a row's arithmetic depends only on its own tokens: the output is
+// bitwise the same whether a sequence runs alone or batched, whatever its
+// physical block IDs or the block size.  512 measured best on the Qwen3
+// decode workload (256 sequences of 100..2048 tokens: 201 us against 207 us
+// at 256 and 236 us at 128): fewer items per wave, half the split-context
+// traffic.  Small batches, whose time is one wave's partition, pay for it
+// (32 Qwen2.5 sequences: 41 us against 27 us at 256).
 #ifndef PA_DECODE_PARTITION
-#define PA_DECODE_PARTITION 256
+#define PA_DECODE_PARTITION PA_DECODE_PARTITION_TOKENS
 #endif
 constexpr int kDecodePartition = PA_DECODE_PARTITION;
 

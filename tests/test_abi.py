@@ -47,8 +47,8 @@ def test_status_strings(lib):
 def test_workspace_bytes(lib):
     assert pa.pa_decode_workspace_bytes(0, 16, 128, 2048) == 0
     n = pa.pa_decode_workspace_bytes(256, 16, 128, 2048)
-    # partials for at least 2048 / 256 partitions of (D outputs + max + sum) per head
-    assert n >= 256 * 16 * 8 * (128 + 2) * 4
+    # partials for at least 2048 / 512 partitions of (D outputs + max + sum) per head
+    assert n >= 256 * 16 * 4 * (128 + 2) * 4
     assert pa.pa_decode_workspace_bytes(1, 1, 64, 1) >= (64 + 2) * 4
 
 
@@ -168,10 +168,19 @@ def test_decode_noalloc_validation(lib):
     assert pa.pa_decode_workspace_bytes(256, 16, 128, 2048) <= binding.NOALLOC_SCRATCH_BYTES
 
 
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    got = {k: v for k, v in re.findall(r"#define\s+(PA_[A-Z_]+)\s+(\d+)\b", src)}
+    assert int(got["PA_DECODE_PARTITION_TOKENS"]) == binding.DECODE_PARTITION_TOKENS
+    assert int(got["PA_PREFILL_WORKSPACE_BYTES"]) == binding.PREFILL_WORKSPACE_BYTES
+    m = re.search(r"#define\s+PA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_workspace_sized_for_its_partitions(lib):
-    # [256 B counter][B*Hq*parts*D fp32, 256-aligned][B*Hq*parts*2 fp32], parts = ceil(L / 256)
+    # [256 B counter][B*Hq*parts*D fp32, 256-aligned][B*Hq*parts*2 fp32], parts = ceil(L / 512)
     B, hq, d, L = 256, 16, 128, 2048
-    parts = -(-L // 256)
+    parts = -(-L // binding.DECODE_PARTITION_TOKENS)
     o = B * hq * parts * d * 4
     ml_off = (256 + o + 255) // 256 * 256
     assert pa.pa_decode_workspace_bytes(B, hq, d, L) == ml_off + B * hq * parts * 2 * 4

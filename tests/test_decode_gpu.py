@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from gpu_harness import assert_close, bits, dev, f64, run_decode, say
+from paged_kv_cache_85_amd.binding import DECODE_PARTITION_TOKENS
 from synth import DecodeSpec, decode_subset, make_case, make_decode
 
 pytestmark = pytest.mark.gpu
@@ -57,18 +58,21 @@ def test_decode_shapes_and_block_sizes(hq, hkv, d, dtype, bs):
     assert_close(f64(out), _oracle(case), dtype, spec.name + f" bs{bs}")
 
 
+P = DECODE_PARTITION_TOKENS   # tokens per decode partition
+
+
 def _sched_lens(kind):
     rng = np.random.default_rng(5)
     if kind == "over-4096-seqs":          # deal tables do not fit LDS: static snake
         lens = rng.integers(1, 8, 4100, endpoint=True)
-        lens[rng.choice(4100, 100, replace=False)] = rng.integers(256, 320, 100, endpoint=True)
+        lens[rng.choice(4100, 100, replace=False)] = rng.integers(P, P + 64, 100, endpoint=True)
         return lens, None
     if kind == "one-partition":           # no workspace: static deal of partial items
-        return rng.integers(1, 256, 300, endpoint=True), 256
+        return rng.integers(1, P, 300, endpoint=True), P
     if kind == "full-only":               # no partial partitions
-        return 256 * rng.integers(1, 8, 200, endpoint=True), None
+        return P * rng.integers(1, 4, 200, endpoint=True), None
     if kind == "partials-only-ticketed":  # workspace present, every item a ticketed partial
-        return rng.integers(1, 255, 300, endpoint=True), 1024
+        return rng.integers(1, P - 1, 300, endpoint=True), 4 * P
     if kind == "few-items":               # fewer items than resident waves
         return np.array([300, 1, 2048]), None
     raise ValueError(kind)
@@ -79,7 +83,7 @@ def _sched_lens(kind):
 def test_decode_deal_paths(kind):
     """The persistent kernel's ways of dealing items (blocks of 64 and 256
     tokens): static snake, tickets, no full or no partial partitions, tiny
-    batches."""
+    batches (lengths chosen against the library's partition size)."""
     lens, max_len = _sched_lens(kind)
     bs = 64 if kind == "over-4096-seqs" else 256   # both take the persistent kernel
     spec = DecodeSpec(f"deal-{kind}", 2, 1, 64, "bf16", bs, context_lens=tuple(int(x) for x in lens))
