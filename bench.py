@@ -142,9 +142,13 @@ COPY_PROBE_BYTES = 1 << 30
 FLUSH_BYTES = 512 << 20
 
 
-def copy_probe(torch, dev) -> None:
-    """A plain copy of known size (1 GiB read, 1 GiB written per launch), run
-    under the same counters as the path so that their bytes can be scaled."""
+def copy_probe(torch, dev, pa=None, up=None, dec=None, stream=None) -> None:
+    """Known-size kernels run under the same counters as the path, so that
+    the counters' bytes can be scaled: a plain elementwise copy (1 GiB read,
+    1 GiB written per launch), and -- for the prefill kernel's
+    direct-to-LDS tile loads -- the decode workload served as varlen rows of
+    one query each, where every key/value tile is read exactly once (bytes
+    in the log line)."""
     src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -153,6 +157,31 @@ def copy_probe(torch, dev) -> None:
     torch.cuda.synchronize()
     log(f"copy probe: 3 x {COPY_PROBE_BYTES} B read + written")
     del src, dst
+    if dec is None:
+        return
+    c = decode_rows_case(dec)
+    kc, vc = up(c.k_cache), up(c.v_cache)
+    pa.pa_store_kv(up(c.k_new), up(c.v_new), kc, vc, up(c.slot_mapping), stream=stream)
+    q = up(c.q)
+    out = torch.empty_like(q)
+    bt, cq, ck = up(c.block_tables), up(c.cu_seqlens_q), up(c.cu_seqlens_k)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        pa.pa_prefill_varlen(out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k,
+                             float(c.scale), stream=stream)
+    torch.cuda.synchronize()
+    log(f"LDS-load probe: 3 x pa_prefill_varlen over {c.num_seqs} one-row sequences, "
+        f"{prefill_bytes(c)} algorithmic bytes each (every key/value tile read once)")
+
+
+def decode_rows_case(dec):
+    """The decode workload's sequences as varlen rows of one query each (the
+    same lengths, heads and block size; fresh seeded contents)."""
+    from synth import PrefillSpec, make_prefill
+    L = dec.context_lens.astype(int)
+    spec = PrefillSpec("decode-rows", dec.num_q_heads, dec.num_kv_heads, dec.head_dim, "bf16",
+                       dec.block_size, q_len_range=(1, 1))
+    return make_prefill(spec, 95, q_lens=(1,) * len(L), prefix_lens=tuple(int(x) - 1 for x in L))
 
 
 def _median_us(torch, fn, stream, reps=20, warm=3):
@@ -255,13 +284,61 @@ def extras(torch, np, pa, dev, up, dec, stream):
         torch.cuda.synchronize()
         return (time.perf_counter() - t) / reps * 1e6
 
+    def wall_synced(fn):
+        # one step at a time, the host waiting for each (a serving loop that
+        # samples every token before it can launch the next step does this)
+        for _ in range(20):
+            fn()
+            torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e6
+
     res["small_decode_step"] = {
         "workload": f"store + decode, {c.num_seqs} sequences, Qwen2.5-0.5B heads, block 16",
         "eager_us_per_step": round(wall(eager), 2),
         "graph_us_per_step": round(wall(g.graph.replay), 2),
+        "eager_us_per_step_synced": round(wall_synced(eager), 2),
+        "graph_us_per_step_synced": round(wall_synced(g.graph.replay), 2),
         "gpu_us_eager": round(_median_us(torch, eager, stream), 2)}
     res["block_manager"] = block_manager_rates(torch, np, pa, dec)
     return res
+
+
+def small_decode_trace(torch, np, pa, dev, up, steps: int) -> None:
+    """The small decode step (store + decode, Qwen2.5-0.5B decode workload,
+    block 16) run `steps` times eagerly, then `steps` graph replays, each
+    group after a synchronisation: under a kernel trace, the dispatch order
+    separates the two groups, so kernel time and the gaps between kernels
+    can be compared."""
+    from synth import make_case
+    from paged_kv_cache_85_amd.graphs import DecodeGraph, bucket_size
+    c = make_case(2)
+    kc, vc = up(c.k_cache), up(c.v_cache)
+    q, kn, vn = up(c.q), up(c.k_new), up(c.v_new)
+    sl, cl, bt = up(c.slot_mapping), up(c.context_lens), up(c.block_tables)
+    out = torch.empty_like(q)
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.head_dim,
+                                                  c.max_context_len), dtype=torch.uint8,
+                     device=dev)
+
+    def eager():
+        pa.pa_store_kv(kn, vn, kc, vc, sl)
+        pa.pa_decode(out, q, kc, vc, bt, cl, c.max_context_len, float(c.scale), workspace=ws)
+
+    g = DecodeGraph(kc, vc, c.num_q_heads, bucket_size(c.num_seqs), bt.shape[1],
+                    c.max_context_len, float(c.scale))
+    g(q, kn, vn, sl, cl, bt)
+    for name, fn in (("eager", eager), ("graph", g.graph.replay)):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"small decode step, {name}: {steps} steps, "
+            f"{(time.perf_counter() - t) / steps * 1e6:.2f} us per step (wall, pipelined)")
 
 
 def block_manager_rates(torch, np, pa, dec):
@@ -328,8 +405,13 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the mixed-batch and graph-replay measurements")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="after the timed steps, run a 1 GiB elementwise copy three times: "
-                         "the known-size kernel that calibrates the HBM byte counters")
+                    help="after the timed steps, run the known-size kernels that calibrate "
+                         "the HBM byte counters: a 1 GiB elementwise copy, and the prefill "
+                         "kernel on one-row sequences (each key/value tile read once), "
+                         "three times each")
+    ap.add_argument("--small-decode-trace", type=int, default=0, metavar="N",
+                    help="only run the small decode step N times eagerly, then N graph "
+                         "replays (for a kernel trace), and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
@@ -353,6 +435,10 @@ def main() -> int:
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
             else torch.from_numpy(a)
         return t.to(dev)
+
+    if args.small_decode_trace:
+        small_decode_trace(torch, np, pa, dev, up, args.small_decode_trace)
+        return 0
 
     log("generating inputs")
     dec = make_case(3)
@@ -454,6 +540,8 @@ def main() -> int:
     dec_path_s = avg["decode"] + avg["store_decode"]
 
     traffic = measured_traffic("decode_qwen3_0.6b")
+    traffic4 = measured_traffic("prefill_varlen_qwen3_0.6b")
+    traffic5 = measured_traffic("prefill_prefix_qwen3_0.6b")
     result = {
         "metric": "paged-attn decode HBM GB/s & prefill TFLOP/s (% of peak), Qwen3-0.6B shapes",
         "value": round(dec_gbs, 2),
@@ -489,12 +577,18 @@ def main() -> int:
             "varlen": {"bound": "mfma", "achieved": round(t4, 2), "peak": BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(t4 / BF16_PEAK_TFLOPS, 4),
                        "flops_per_launch": f4, "avg_launch_us": round(avg["prefill"] * 1e6, 2),
+                       "algorithmic_bytes_per_launch": prefill_bytes(pre4),
+                       "traffic": traffic4,
                        "hbm_frac": round(prefill_bytes(pre4) / avg["prefill"] / 1e9
-                                         / HBM_PEAK_GBS, 4)},
+                                         / HBM_PEAK_GBS, 4),
+                       "hbm_frac_measured": None if traffic4 is None else
+                       round(traffic4 / avg["prefill"] / 1e9 / HBM_PEAK_GBS, 4)},
             "prefix_cache": {"bound": "mfma", "achieved": round(t5, 2),
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(t5 / BF16_PEAK_TFLOPS, 4), "flops_per_launch": f5,
-                             "avg_launch_us": round(avg["prefix_prefill"] * 1e6, 2)},
+                             "avg_launch_us": round(avg["prefix_prefill"] * 1e6, 2),
+                             "algorithmic_bytes_per_launch": prefill_bytes(pre5),
+                             "traffic": traffic5},
             "median": {"varlen_tflops": round(f4 / med["prefill"] / 1e12, 2),
                        "prefix_cache_tflops": round(f5 / med["prefix_prefill"] / 1e12, 2),
                        "decode_gbs": round(dec_bytes / med["decode"] / 1e9, 2)},
@@ -517,7 +611,7 @@ def main() -> int:
         del D, P4, P5
         result["next_rows"] = extras(torch, np, pa, dev, up, dec, stream)
     if args.copy_probe:
-        copy_probe(torch, dev)
+        copy_probe(torch, dev, pa, up, dec, stream)
     print(json.dumps(result), flush=True)
     return 0
 

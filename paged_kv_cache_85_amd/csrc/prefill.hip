@@ -186,10 +186,18 @@ __device__ __forceinline__ bool walk_to(ItemWalk& wk, int k, const uint16_t* nti
   return false;
 }
 
-// BN keys per tile, NST tile stages in LDS.  NT: the tiles stream with the
-// non-temporal cache policy (launches of decode rows only, whose tiles are
-// read once).
-template <int D, int HPW, bool DMA, int BN, int NST, bool NT>
+// Cache policy of the key/value tiles.  Tiles of a sequence with several
+// query rows are re-read through L2 by its other query tiles and heads; a
+// decode row (one query row) reads each of its tiles once, so those stream
+// with the non-temporal policy.
+enum TilePolicy : int {
+  kTilesCached = 0,    // every item: default policy
+  kTilesStreamed = 1,  // every item is a decode row: non-temporal
+  kTilesPerItem = 2,   // mixed batches: non-temporal for items of one query row
+};
+
+// BN keys per tile, NST tile stages in LDS, POL a TilePolicy.
+template <int D, int HPW, bool DMA, int BN, int NST, int POL>
 __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k) {
@@ -370,6 +378,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
 
   // Request tile kt, which lies in physical block blk_id, into stage buffers
   // (dk, dv).  Rows past Lk lie outside the descriptors and arrive as zeros.
+  const bool stream_tiles = POL == kTilesStreamed || (POL == kTilesPerItem && Lq == 1);
   auto request = [&](uint16_t* dk, uint16_t* dv, int kt, int blk_id) __attribute__((always_inline)) {
     const int t0 = kt * BN;
     const int blk = clamp_block(blk_id, nblk);
@@ -377,10 +386,17 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
     const u32x4 rk = stream_rsrc(kcache + base, bytes);
     const u32x4 rv = stream_rsrc(vcache + base, bytes);
+    if (stream_tiles) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16<NT>(rk, dk + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<true>(rk, dk + (w * NI + i) * 512, src_off[i]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_load16<NT>(rv, dv + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<true>(rv, dv + (w * NI + i) * 512, src_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_load16<false>(rk, dk + (w * NI + i) * 512, src_off[i]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_load16<false>(rv, dv + (w * NI + i) * 512, src_off[i]);
+    }
   };
 
   // Other block sizes: the same chunks through registers, each row looked up
@@ -663,21 +679,21 @@ static bool xcd_groups_ok(const PrefillArgs& a, int bmq) {
   return (long long)a.total_q >= 2LL * bmq * a.num_seqs;
 }
 
-template <int D, int HPW, bool DMA, bool NT>
+template <int D, int HPW, bool DMA, int POL>
 static int launch_items(const PrefillArgs& a, long long n_items, hipStream_t stream) {
   constexpr int BN = PA_PREFILL_BN;
   constexpr int NST = PA_PREFILL_NST;
   constexpr int BMQ = 32 * (4 / HPW);
   static std::atomic<int> slots_cache[kMaxDevices];
   const int slots = resident_blocks(
-      reinterpret_cast<const void*>(prefill_bf16_kernel<D, HPW, DMA, BN, NST, NT>), 256,
+      reinterpret_cast<const void*>(prefill_bf16_kernel<D, HPW, DMA, BN, NST, POL>), 256,
       slots_cache);
   if (slots < 0) return -1;
   PrefillArgs p = a;
   p.persistent = persistent_ok(a, n_items, slots, BMQ) ? 1 : 0;
   p.xcd_groups = xcd_groups_ok(a, BMQ) ? 1 : 0;
   const long long grid = p.persistent ? slots : n_items;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST, NT>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, HPW, DMA, BN, NST, POL>), dim3((unsigned)grid),
                      dim3(256), 0, stream, p, a.block_tables, a.cu_seqlens_q, a.cu_seqlens_k);
   return 0;
 }
@@ -694,11 +710,19 @@ static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
     // Tiles inside one block.  When every query row is a decode row (one
     // row per sequence), each key/value tile is read by a single item:
     // those launches stream the tiles past the caches, as decode does; any
-    // longer query tile re-reads its sequence's tiles through L2.
-    if (a.max_seqlen_q == 1) return launch_items<D, HPW, true, true>(a, n_items, stream);
-    return launch_items<D, HPW, true, false>(a, n_items, stream);
+    // longer query tile re-reads its sequence's tiles through L2.  A batch
+    // whose sequences average less than one query tile each is taken for
+    // a mixed one (decode rows beside a few prompts): its items choose
+    // their policy one by one.  (Per-item choice on prompt-only batches
+    // measured 2.5 % slower on the prefix-cache workload, so they keep one
+    // policy for the launch.)
+    if (a.max_seqlen_q == 1)
+      return launch_items<D, HPW, true, kTilesStreamed>(a, n_items, stream);
+    if ((long long)a.total_q < (long long)BMQ * a.num_seqs)
+      return launch_items<D, HPW, true, kTilesPerItem>(a, n_items, stream);
+    return launch_items<D, HPW, true, kTilesCached>(a, n_items, stream);
   }
-  return launch_items<D, HPW, false, false>(a, n_items, stream);
+  return launch_items<D, HPW, false, kTilesCached>(a, n_items, stream);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
