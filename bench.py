@@ -70,14 +70,24 @@ def prefill_bytes(case) -> int:
     return qo + 2 * keys * case.num_kv_heads * case.head_dim * e
 
 
+def _code_only(src: str) -> str:
+    """C/C++ source without comments and whitespace: what the compiler sees,
+    so that an edit to comments alone keeps a measurement's digest."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return re.sub(r"\s+", "", src)
+
+
 def kernel_sources_digest(files=None) -> str:
     """Digest of the kernel sources a measurement depends on (all of csrc/ by
-    default), so that a counter summary taken on other sources is not used."""
+    default; comments and whitespace ignored), so that a counter summary
+    taken on other code is not used."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_85_amd", "csrc")
     for f in sorted(files if files else os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

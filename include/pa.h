@@ -177,8 +177,8 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * cu_seqlens_k[b+1] - cu_seqlens_k[b] keys, all read from the pools through
  * block_tables[b] (store the new rows with pa_store_kv first).  The new rows
  * are the last Lq tokens of the sequence, so row i attends to keys
- * 0 .. (Lk - Lq) + i ("mini-vLLM", project summary: each packed prompt
- * attends causally to itself; the smzdm Nano-vLLM walk-through, model
+ * 0 .. (Lk - Lq) + i ("mini-vLLM", project summary: a row of a packed
+ * prompt sees its own prompt up to its own position; the smzdm Nano-vLLM walk-through, model
  * implementation details: cu_seqlens_k > cu_seqlens_q marks a prefix-cache
  * hit).
  *   out, q        [total_q, num_q_heads, head_dim] packed
@@ -247,9 +247,9 @@ int pa_qk_norm_rope_store(void* q_out, const void* q, const void* k, const void*
 /*
  * Host block manager: the CPU bookkeeping that produces the kernels' paging
  * inputs ("nano-vLLM Part 4", section 1: block IDs, reference counts and
- * prefix-hash metadata live on the CPU; "mini-vLLM", features list: a fixed
- * pool of blocks with an O(1) free-list allocator and a block table per
- * sequence).  Full blocks are registered under their token content chained
+ * prefix-hash metadata live on the CPU; "mini-vLLM", features list: blocks
+ * come from a pool fixed at start-up, taken and returned in constant time,
+ * and each sequence keeps a table of the blocks it owns).  Full blocks are registered under their token content chained
  * with their predecessor, so a sequence starting with the same full blocks
  * shares them (reference counts) -- an exact full-block prefix cache (smzdm
  * Nano-vLLM walk-through, scheduling and memory).  A freed block keeps its

@@ -7,8 +7,8 @@ tests may use it, and it shares no code with the C++ manager in libpa.
 What it models, and where the pages say so:
 
 * a fixed pool of equal blocks handed out from a free list, first in first
-  out ("mini-vLLM", features list: an O(1) free-list allocator; a block table
-  per sequence);
+  out ("mini-vLLM", features list: constant-time block hand-out from a pool
+  fixed at start-up; every sequence keeps its own table of blocks);
 * full blocks registered by their content so that a sequence beginning with
   the same full blocks shares them, with reference counts (smzdm Nano-vLLM
   walk-through, scheduling and memory: the shared system prompt is reused;

@@ -18,8 +18,9 @@ What it computes, and where the pages say so:
 * decode -- one query token per sequence attends to that sequence's whole
   cached history ("mini-vLLM", project summary; "nano-vLLM Part 4", section 3:
   decode attention runs over the cached history through the block table).
-* varlen prefill -- packed prompts, each attending causally to itself
-  ("mini-vLLM", project summary).  When a sequence has more keys than new
+* varlen prefill -- prompts laid end to end in one batch; a row sees only
+  keys of its own prompt at or before its own position ("mini-vLLM", project
+  summary).  When a sequence has more keys than new
   queries (cu_seqlens_k > cu_seqlens_q: a prefix-cache hit, smzdm walk-through,
   model implementation details) the new rows are the LAST rows of the
   sequence, so row i sees keys 0 .. (Lk - Lq) + i (bottom-right alignment).

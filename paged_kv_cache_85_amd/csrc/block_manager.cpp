@@ -5,7 +5,7 @@
 // The engines keep this state on the CPU ("nano-vLLM Part 4", section 1: the
 // block manager holds block IDs, reference counts and prefix-hash metadata,
 // none of it in GPU memory).  The pool is a fixed set of equal blocks handed
-// out by an O(1) free list ("mini-vLLM", features list); full blocks are
+// out and returned in constant time ("mini-vLLM", features list); full blocks are
 // registered under a hash of their tokens chained with the previous block's
 // hash, so a new sequence that starts with the same full blocks reuses them
 // with a reference count (smzdm Nano-vLLM walk-through, scheduling and memory:

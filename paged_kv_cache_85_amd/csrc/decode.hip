@@ -1,9 +1,9 @@
 // Decode attention over a paged KV cache on the vector ALUs, split over the
 // context with an online softmax.
 //
-// A decode query is one token per sequence attending to that sequence's
-// cached keys and values ("mini-vLLM", project summary), read through the
-// sequence's block table ("nano-vLLM Part 4", section 3: decode attention
+// In a decode step every sequence contributes a single new query row, and
+// that row looks at all of its own sequence's cached keys and values
+// ("mini-vLLM", project summary), fetched through the sequence's block table ("nano-vLLM Part 4", section 3: decode attention
 // over the cached history).  The work is HBM-bound (about 2 FLOP per byte of
 // bf16 KV at a query group of 2), so the kernels are organised around the
 // memory stream, not the matrix cores:

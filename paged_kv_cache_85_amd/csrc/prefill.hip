@@ -1,8 +1,8 @@
 // Varlen causal prefill over a paged KV cache on the gfx950 matrix cores
 // (bf16 inputs, fp32 accumulation).
 //
-// Packed prompts attend causally to themselves ("mini-vLLM", project
-// summary); sequence boundaries come from cu_seqlens_q / cu_seqlens_k, and
+// Prompts are packed end to end; each row sees its own prompt up to its own
+// position ("mini-vLLM", project summary); sequence boundaries come from cu_seqlens_q / cu_seqlens_k, and
 // cu_seqlens_k > cu_seqlens_q means the sequence already has a cached prefix
 // (smzdm Nano-vLLM walk-through, model implementation details), so its Lq new
 // rows are the last rows of the sequence: row i sees keys 0 .. Lk - Lq + i.
