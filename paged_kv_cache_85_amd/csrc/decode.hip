@@ -27,7 +27,7 @@
 //    block IDs and the block size.
 //
 // Large power-of-two blocks (>= 64 tokens; 256 in the Qwen3 workloads) run a
-// persistent kernel: one wave per resident slot walks an equal, contiguous
+// persistent kernel: one wave per SIMD walks an equal, contiguous
 // share of all items, and a ring of register stages keeps NBUF - 1 stages in
 // flight across item boundaries, so the memory stream never drains between
 // items and no launch slot is spent on empty partitions.  Each stage is read
@@ -968,14 +968,20 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
 
 template <typename E, int D, int HG>
 static int launch_persistent(const RowAttnArgs& a, hipStream_t stream) {
-  // One wave per resident slot: CUs x the kernel's occupancy.
+  // One wave per SIMD (never more than the kernel's occupancy allows).  Two
+  // waves sharing a SIMD split its memory stream unevenly -- the older wave's
+  // requests go first, and on the Qwen3 decode workload the younger one took
+  // 2.6x as long over the same item, which left a long tail -- while one
+  // wave per SIMD with two stages in flight already keeps HBM saturated.
   static std::atomic<int> slots_cache[kMaxDevices];
-  const int cached_waves = resident_blocks(
+  static std::atomic<int> simds_cache[kMaxDevices];
+  const int resident = resident_blocks(
       reinterpret_cast<const void*>(decode_persistent_kernel<E, D, HG>), 64, slots_cache);
-  if (cached_waves < 0) return -1;
+  const int simds = device_simds(simds_cache);
+  if (resident < 0 || simds < 0) return -1;
   const long long max_items =
       (long long)a.num_rows * a.num_kv_heads * a.head_chunks * a.max_parts;
-  const int waves = (int)min((long long)cached_waves, max_items);
+  const int waves = (int)min((long long)min(resident, simds), max_items);
   if (waves <= 0) return 0;
   hipLaunchKernelGGL((decode_persistent_kernel<E, D, HG>), dim3(waves), dim3(64), 0, stream, a,
                      a.context_lens, a.block_tables);

@@ -114,6 +114,24 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
 // table needs no lock.  Devices past kMaxDevices are queried on every call.
 constexpr int kMaxDevices = 64;
 
+// SIMDs of the current device (4 per CU on this architecture), cached like
+// resident_blocks.
+inline int device_simds(std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  const int v = 4 * (cus > 0 ? cus : 1);
+  if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 inline int resident_blocks(const void* kernel, int threads, std::atomic<int>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
