@@ -255,7 +255,6 @@ struct RowFold {
   }
 };
 
-__device__ __forceinline__ int num_parts(int L, int P) { return L > 0 ? (L + P - 1) / P : 0; }
 
 // ---------------------------------------------------------------- one wave per item
 //
@@ -1043,7 +1042,18 @@ static int dispatch_rows(const RowAttnArgs& a, int head_dim, int dtype, bool var
 }
 
 int launch_decode(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream) {
-  int rc = dispatch_rows(a, head_dim, dtype, false, stream);
+  // bf16 query groups of kGqaMfmaMinGroup heads or more fold on the matrix
+  // cores (every block size, so results stay independent of it).
+  const int mfma_heads = dtype == 1 ? gqa_mfma_heads(a.group, head_dim) : 0;
+  int rc;
+  if (mfma_heads > 0) {
+    RowAttnArgs m = a;
+    m.heads_per_wg = mfma_heads;
+    m.head_chunks = a.group / mfma_heads;
+    rc = launch_decode_gqa_mfma(m, head_dim, stream);
+  } else {
+    rc = dispatch_rows(a, head_dim, dtype, false, stream);
+  }
   if (rc || a.max_parts <= 1) return rc;
   const dim3 g((unsigned)((long long)a.num_rows * a.num_q_heads));
   if (dtype == 0) {

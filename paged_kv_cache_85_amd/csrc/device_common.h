@@ -103,6 +103,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // real score m, and exp2(kNegBig - kNegBig) is 1, so no NaN arises.
 constexpr float kNegBig = -1.0e30f;
 
+// Context partitions of a row of L tokens (P tokens each).
+__device__ __forceinline__ int num_parts(int L, int P) { return L > 0 ? (L + P - 1) / P : 0; }
+
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
   return min(max(blk, 0), num_blocks - 1);
 }

@@ -107,6 +107,43 @@ def test_decode_block_size_invariance_bitwise():
         assert np.array_equal(o, outs[0])
 
 
+GQA_SHAPES = [(14, 2, 64), (16, 1, 128), (32, 2, 64), (32, 1, 64), (8, 2, 128), (12, 3, 64)]
+
+
+@pytest.mark.parametrize("hq,hkv,d", GQA_SHAPES)
+def test_decode_large_groups_block_size_invariance_bitwise(hq, hkv, d):
+    """Query groups of 4 and more run on the matrix cores for every block
+    size: identical bits across block sizes, and the oracle within the bf16
+    bar (groups 4, 7, 16; 32 = two chunks of 16 heads)."""
+    spec = DecodeSpec(f"dec-gqa-{hq}-{hkv}-{d}", hq, hkv, d, "bf16", 16,
+                      context_lens=(1, 2, 31, 32, 33, 100, 511, 512, 513, 1100))
+    outs = []
+    for bs in (1, 3, 16, 64, 256):
+        case = make_decode(spec, 91, block_size=bs)
+        out, _, _ = run_decode(case)
+        if bs == 16:
+            assert_close(f64(out), _oracle(case), "bf16", spec.name)
+        outs.append(bits(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_decode_large_group_batching_bitwise():
+    """The 32-sequence Qwen2.5 batch (group 7): permuted block IDs, each
+    sequence alone and the batch reversed give the same bits."""
+    case = make_case(2)
+    ref = bits(run_decode(case)[0])
+    assert np.array_equal(bits(run_decode(make_case(2, perm_seed=17))[0]), ref)
+    for b in (0, 13, 31):
+        alone, _, _ = run_decode(decode_subset(case, [b], perm_seed=b + 3,
+                                               table_width=case.max_blocks_per_seq),
+                                 max_context_len=case.max_context_len)
+        assert np.array_equal(bits(alone)[0], ref[b]), b
+    rev = list(range(case.num_seqs))[::-1]
+    out, _, _ = run_decode(decode_subset(case, rev, perm_seed=8))
+    assert np.array_equal(bits(out)[::-1], ref)
+
+
 def test_decode_permutation_and_batching_bitwise():
     case = make_case(2)
     ref, _, _ = run_decode(case)
