@@ -25,9 +25,13 @@
 //
 // The unit of work, the partition size, the partial format and the combine
 // are those of the vector kernels: an item is (sequence, 512-token
-// partition, KV head [, chunk of 16 heads]), one wave per item, and a
-// sequence with several partitions writes unnormalised partials that the
-// combine kernel merges in partition order.  A row's arithmetic depends only
+// partition, KV head [, chunk of 16 heads]), and a sequence with several
+// partitions writes unnormalised partials that the combine kernel merges in
+// partition order.  A workgroup of NW waves folds an item: wave w takes the
+// w-th fixed quarter (part_tokens / NW tokens) of the partition, and the
+// quarters' states are merged through LDS in wave order -- a fixed split, so
+// a small batch gets NW times the waves without any change to a row's
+// arithmetic.  A row's arithmetic depends only
 // on its own tokens: results are bitwise independent of the batch, the
 // physical block IDs and the block size (the block table is staged in LDS
 // and every block size takes this kernel).
@@ -66,9 +70,10 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
 
 }  // namespace
 
-// D: head dim (64 or 128); NST: register stages in the ring.
-template <int D, int NST>
-__global__ __launch_bounds__(64) void decode_gqa_mfma_kernel(RowAttnArgs a) {
+// D: head dim (64 or 128); NST: register stages in the ring; NW: waves per
+// item.
+template <int D, int NST, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_gqa_mfma_kernel(RowAttnArgs a) {
   constexpr int KC = D / 32;            // 32-dim chunks of the score products
   constexpr int NBD = D / 16;           // 16-dim blocks of the output products
   constexpr int CPR = D / 8;            // 16-byte chunks per head row
@@ -76,7 +81,8 @@ __global__ __launch_bounds__(64) void decode_gqa_mfma_kernel(RowAttnArgs a) {
   constexpr int RS = D + (D == 64 ? 8 : 16);  // LDS row stride (elements), padded for the transpose reads
   constexpr int CH = 32;                // tokens per chunk
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;      // wave of the item
   const int col = lane & 15;            // head column
   const int grp = lane >> 4;            // lane group: k rows 8*grp .. 8*grp + 7
 
@@ -95,26 +101,33 @@ __global__ __launch_bounds__(64) void decode_gqa_mfma_kernel(RowAttnArgs a) {
   const int L = min(a.context_lens[row], a.max_context);
   if (L <= 0) {  // violated precondition: define the output as zeros
     if (p == 0)
-      for (int idx = lane; idx < HG * D; idx += 64)
+      for (int idx = threadIdx.x; idx < HG * D; idx += 64 * NW)
         out[((long)row * a.num_q_heads + h0) * D + idx] = 0;
     return;
   }
   const int nparts = num_parts(L, a.part_tokens);
   if (p >= nparts) return;
-  const int tok_begin = p * a.part_tokens;
-  const int tok_end = min(L, tok_begin + a.part_tokens);
+  const int part_begin = p * a.part_tokens;
+  const int part_end = min(L, part_begin + a.part_tokens);
+  // This wave's quarter of the partition (possibly empty).
+  const int quarter = a.part_tokens / NW;
+  const int tok_begin = part_begin + wv * quarter;
+  const int tok_end = min(part_end, tok_begin + quarter);
   const int32_t* bt = a.block_tables + (long)row * a.max_blocks_per_seq;
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nb = a.num_blocks;
 
-  // The partition's block IDs, clamped into the pool.
+  // The partition's block IDs, clamped into the pool; each wave's V staging
+  // rows; the quarters' states for the merge.
   __shared__ int s_bt[kDecodePartition];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[CH * RS];
-  const int first_blk = bs_log2 >= 0 ? (tok_begin >> bs_log2) : tok_begin / bs;
+  __shared__ __attribute__((aligned(16))) uint16_t s_vall[NW][CH * RS];
+  __shared__ float s_state[NW - 1][D / 4 + 2][64];
+  uint16_t* s_v = s_vall[wv];
+  const int first_blk = bs_log2 >= 0 ? (part_begin >> bs_log2) : part_begin / bs;
   {
-    const int last_blk = bs_log2 >= 0 ? ((tok_end - 1) >> bs_log2) : (tok_end - 1) / bs;
-    for (int i = lane; i <= last_blk - first_blk && i < kDecodePartition; i += 64)
+    const int last_blk = bs_log2 >= 0 ? ((part_end - 1) >> bs_log2) : (part_end - 1) / bs;
+    for (int i = threadIdx.x; i <= last_blk - first_blk && i < kDecodePartition; i += 64 * NW)
       s_bt[i] = clamp_block(bt[first_blk + i], nb);
     __syncthreads();
   }
@@ -239,22 +252,59 @@ __global__ __launch_bounds__(64) void decode_gqa_mfma_kernel(RowAttnArgs a) {
 
   // Ring of NST register stages (NST - 1 chunks in flight while one is
   // folded); past the last chunk the loads repeat the last chunk.
-  u32x4m kbuf[NST][2][KC], vbuf[NST][VL];
-  const int last_c0 = tok_begin + ((tok_end - tok_begin - 1) / CH) * CH;
-  int c0 = tok_begin;
+  if (tok_begin < tok_end) {
+    u32x4m kbuf[NST][2][KC], vbuf[NST][VL];
+    const int last_c0 = tok_begin + ((tok_end - tok_begin - 1) / CH) * CH;
+    int c0 = tok_begin;
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) load(kbuf[i], vbuf[i], min(c0 + i * CH, last_c0));
-  for (;;) {
+    for (int i = 0; i < NST - 1; ++i) load(kbuf[i], vbuf[i], min(c0 + i * CH, last_c0));
+    for (;;) {
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      load(kbuf[(i + NST - 1) % NST], vbuf[(i + NST - 1) % NST], min(c0 + (NST - 1) * CH, last_c0));
-      __builtin_amdgcn_sched_barrier(0);
-      fold(kbuf[i], vbuf[i], c0);
-      if (c0 >= last_c0) goto folded;
-      c0 += CH;
+      for (int i = 0; i < NST; ++i) {
+        load(kbuf[(i + NST - 1) % NST], vbuf[(i + NST - 1) % NST],
+             min(c0 + (NST - 1) * CH, last_c0));
+        __builtin_amdgcn_sched_barrier(0);
+        fold(kbuf[i], vbuf[i], c0);
+        if (c0 >= last_c0) goto folded;
+        c0 += CH;
+      }
     }
   }
 folded:
+  // Merge the quarters in wave order: M = max of the quarters' maxima, then
+  // O and the lane sums rescaled to M and summed wave 0 first.  (An empty
+  // quarter has max kNegBig and weight 0.)
+  if (wv > 0) {
+#pragma unroll
+    for (int n = 0; n < NBD; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_state[wv - 1][4 * n + e][lane] = oacc[n][e];
+    s_state[wv - 1][D / 4][lane] = m_run;
+    s_state[wv - 1][D / 4 + 1][lane] = l_lane;
+  }
+  __syncthreads();
+  if (wv > 0) return;
+  {
+    float M = m_run;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_state[w - 1][D / 4][lane]);
+    const float w0 = fast_exp2(m_run - M);
+#pragma unroll
+    for (int n = 0; n < NBD; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[n][e] *= w0;
+    l_lane *= w0;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float ww = fast_exp2(s_state[w - 1][D / 4][lane] - M);
+#pragma unroll
+      for (int n = 0; n < NBD; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[n][e] = fmaf(s_state[w - 1][4 * n + e][lane], ww, oacc[n][e]);
+      l_lane = fmaf(s_state[w - 1][D / 4 + 1][lane], ww, l_lane);
+    }
+    m_run = M;
+  }
   // Output: lane (col, grp) holds head col's dims 16 * n + 4 * grp + e.
   {
     const float l_tot = sum_across_groups(l_lane);
@@ -292,6 +342,10 @@ int gqa_mfma_heads(int group, int head_dim) {
   return 0;
 }
 
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+constexpr int kGqaWaves = PA_GQA_WAVES;  // waves (fixed token quarters) per item
 #ifndef PA_GQA_STAGES_D64
 #define PA_GQA_STAGES_D64 3
 #endif
@@ -304,10 +358,13 @@ int launch_decode_gqa_mfma(const RowAttnArgs& a, int head_dim, hipStream_t strea
       (long long)a.num_rows * a.num_kv_heads * a.head_chunks * a.max_parts;
   if (grid <= 0) return 0;
   if (grid > 0x7fffffffLL) return -1;
+  static_assert(kDecodePartition % (32 * kGqaWaves) == 0, "partition quarters hold whole chunks");
   if (head_dim == 64)
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<64, PA_GQA_STAGES_D64>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<64, PA_GQA_STAGES_D64, kGqaWaves>),
+                       dim3((unsigned)grid), dim3(64 * kGqaWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<128, PA_GQA_STAGES_D128>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<128, PA_GQA_STAGES_D128, kGqaWaves>),
+                       dim3((unsigned)grid), dim3(64 * kGqaWaves), 0, stream, a);
   return 0;
 }
 
