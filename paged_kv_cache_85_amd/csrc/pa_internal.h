@@ -72,7 +72,10 @@ struct RowAttnArgs {
 
 int launch_decode(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream);
 // Query groups from this size up take the matrix-core decode kernel (bf16).
-constexpr int kGqaMfmaMinGroup = 4;
+#ifndef PA_GQA_MIN_GROUP
+#define PA_GQA_MIN_GROUP 4
+#endif
+constexpr int kGqaMfmaMinGroup = PA_GQA_MIN_GROUP;
 int gqa_mfma_heads(int group, int head_dim);
 int launch_decode_gqa_mfma(const RowAttnArgs& a, int head_dim, hipStream_t stream);
 int launch_varlen_rows(const RowAttnArgs& a, int head_dim, int dtype, hipStream_t stream);
