@@ -120,6 +120,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   context_lens  int32 [num_seqs]
  *   head_dim      64 or 128
  *   max_context_len  host upper bound of context_lens (sizes the grid)
+ *   bf16 query groups of 4 or more heads (G >= 4) run on the matrix cores,
+ *   other shapes and fp32 on the vector ALUs; the choice depends only on
+ *   (dtype, head_dim, G), so a row's result never depends on the batch, the
+ *   block size or the physical block IDs.
  *   workspace     device memory of at least
  *                 pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
  *                 max_context_len) bytes, 256-byte aligned.  Its first 256
