@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import assert_close, bits, dev, f64, run_decode, say
+from gpu_harness import assert_close, bits, dev, f64, run_decode, run_store, say
 from paged_kv_cache_85_amd.binding import DECODE_PARTITION_TOKENS
 from synth import DecodeSpec, decode_subset, make_case, make_decode
 
@@ -126,6 +126,42 @@ def test_decode_large_groups_block_size_invariance_bitwise(hq, hkv, d):
         outs.append(bits(out))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+def test_decode_large_group_long_contexts():
+    """Matrix-core path over long contexts (up to 17 partitions merged by the
+    combine kernel), a one-token row, and a host bound above every length."""
+    spec = DecodeSpec("dec-gqa-long", 14, 2, 64, "bf16", 16,
+                      context_lens=(8193, 1, 4096, 8192, 511, 6000))
+    case = make_decode(spec, 93)
+    case = decode_subset(case, range(case.num_seqs), table_width=-(-9000 // 16))
+    out, _, _ = run_decode(case, max_context_len=9000)
+    assert_close(f64(out), _oracle(case), "bf16", spec.name)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [(16, 8, 128, 256), (16, 8, 128, 16), (14, 2, 64, 16)])
+def test_decode_zero_length_row_gives_zeros(hq, hkv, d, bs):
+    """A row whose length violates the precondition (0) comes out as zeros on
+    every path (persistent, one wave per item, matrix cores); the other rows
+    are untouched by it (PA_CHECK off)."""
+    import torch
+    import paged_kv_cache_85_amd as pa
+    spec = DecodeSpec(f"dec-zero-{hq}-{hkv}-{bs}", hq, hkv, d, "bf16", bs,
+                      context_lens=(700, 33, 1200, 5))
+    case = make_decode(spec, 95)
+    kc, vc = run_store(case)
+    q = dev(case.q)
+    lens = case.context_lens.copy()
+    lens[1] = 0
+    out = torch.full_like(q, float("nan"))
+    pa.pa_decode(out, q, kc, vc, dev(case.block_tables), dev(lens), case.max_context_len,
+                 float(case.scale))
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.all(got[1] == 0.0)
+    ref = _oracle(case)
+    keep = [0, 2, 3]
+    assert_close(got[keep], ref[keep], "bf16", spec.name)
 
 
 def test_decode_large_group_batching_bitwise():
