@@ -31,10 +31,10 @@
 // w-th fixed quarter (part_tokens / NW tokens) of the partition, and the
 // quarters' states are merged through LDS in wave order -- a fixed split, so
 // a small batch gets NW times the waves without any change to a row's
-// arithmetic.  A row's arithmetic depends only
-// on its own tokens: results are bitwise independent of the batch, the
-// physical block IDs and the block size (the block table is staged in LDS
-// and every block size takes this kernel).
+// arithmetic.  A row's arithmetic depends only on its own tokens: results
+// are bitwise independent of the batch, the physical block IDs and the block
+// size (the block table is staged in LDS and every block size takes this
+// kernel).
 #include "device_common.h"
 #include "pa_internal.h"
 
