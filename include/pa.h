@@ -113,9 +113,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * Decode: out[b, h, :] = softmax_j(scale * <q[b, h], K_b[j, h / G]>) . V_b[j, h / G]
  * over the context_lens[b] tokens of sequence b (which include the token just
  * stored), where K_b / V_b are gathered through block_tables[b] and
- * G = num_q_heads / num_kv_heads ("mini-vLLM", project summary: a decode token
- * attends to its sequence's cached keys and values; "nano-vLLM Part 4",
- * section 3: decode attention runs over the cached history).
+ * G = num_q_heads / num_kv_heads ("mini-vLLM", project summary: in decode each
+ * sequence adds one query row, scored against that sequence's stored history;
+ * "nano-vLLM Part 4", section 3: decode attention runs over the cached history).
  *   out, q        [num_seqs, num_q_heads, head_dim]
  *   context_lens  int32 [num_seqs]
  *   head_dim      64 or 128

@@ -1,10 +1,10 @@
 // Decode attention over a paged KV cache on the vector ALUs, split over the
 // context with an online softmax.
 //
-// In a decode step every sequence contributes a single new query row, and
-// that row looks at all of its own sequence's cached keys and values
-// ("mini-vLLM", project summary), fetched through the sequence's block table ("nano-vLLM Part 4", section 3: decode attention
-// over the cached history).  The work is HBM-bound (about 2 FLOP per byte of
+// A decode step scores one new query row per sequence against the whole
+// stored history of that sequence ("mini-vLLM", project summary), read
+// through the sequence's block table ("nano-vLLM Part 4", section 3: decode
+// attention over the cached history).  The work is HBM-bound (about 2 FLOP per byte of
 // bf16 KV at a query group of 2), so the kernels are organised around the
 // memory stream, not the matrix cores:
 //

@@ -3,9 +3,9 @@ prompts (with or without a cached prefix) served by one pa_prefill_varlen
 launch, against the fp64 oracle.
 
 A decode row is a varlen sequence with Lq = 1 and Lk = its context length, so
-the same call covers both phases ("mini-vLLM", project summary: decode is one
-token per sequence attending to its cache; prefill packs prompts, each causal
-to itself).  Parity bar as elsewhere: bf16 max-abs <= 2e-2 and mean-abs <=
+the same call covers both phases ("mini-vLLM", project summary: a decode row
+is one new query per sequence over its stored history, and a prefill packs
+several prompts whose rows see only earlier positions of their own prompt).  Parity bar as elsewhere: bf16 max-abs <= 2e-2 and mean-abs <=
 2e-3, fp32 max-abs <= 1e-5.
 """
 import numpy as np
