@@ -97,39 +97,28 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_mfma_kernel(RowAttnArgs a)
   const int g = y / a.head_chunks;
   const int h0 = g * a.group + (y % a.head_chunks) * HG;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-
-  const int L = min(a.context_lens[row], a.max_context);
-  if (L <= 0) {  // violated precondition: define the output as zeros
-    if (p == 0)
-      for (int idx = threadIdx.x; idx < HG * D; idx += 64 * NW)
-        out[((long)row * a.num_q_heads + h0) * D + idx] = 0;
-    return;
-  }
-  const int nparts = num_parts(L, a.part_tokens);
-  if (p >= nparts) return;
-  const int part_begin = p * a.part_tokens;
-  const int part_end = min(L, part_begin + a.part_tokens);
-  // This wave's quarter of the partition (possibly empty).
-  const int quarter = a.part_tokens / NW;
-  const int tok_begin = part_begin + wv * quarter;
-  const int tok_end = min(part_end, tok_begin + quarter);
   const int32_t* bt = a.block_tables + (long)row * a.max_blocks_per_seq;
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nb = a.num_blocks;
-
-  // The partition's block IDs, clamped into the pool; each wave's V staging
-  // rows; the quarters' states for the merge.
-  __shared__ int s_bt[kDecodePartition];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vall[NW][CH * RS];
-  __shared__ float s_state[NW - 1][D / 4 + 2][64];
-  uint16_t* s_v = s_vall[wv];
+  const int part_begin = p * a.part_tokens;
   const int first_blk = bs_log2 >= 0 ? (part_begin >> bs_log2) : part_begin / bs;
+
+  // The block IDs of the partition's whole span (within the table's width)
+  // and the query are loaded together with the sequence length, so that one
+  // memory round trip, not three, precedes the key/value loads.  Entries
+  // past the sequence's end are staged too (clamped) and never used.
+  constexpr int BPT = (kDecodePartition + 64 * NW - 1) / (64 * NW);
+  int btv[BPT];
   {
-    const int last_blk = bs_log2 >= 0 ? ((part_end - 1) >> bs_log2) : (part_end - 1) / bs;
-    for (int i = threadIdx.x; i <= last_blk - first_blk && i < kDecodePartition; i += 64 * NW)
-      s_bt[i] = clamp_block(bt[first_blk + i], nb);
-    __syncthreads();
+    const int span_end = part_begin + a.part_tokens - 1;
+    const int last_span = bs_log2 >= 0 ? (span_end >> bs_log2) : span_end / bs;
+    const int nspan = min(min(last_span, a.max_blocks_per_seq - 1) - first_blk + 1, kDecodePartition);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int i = (int)threadIdx.x + k * 64 * NW;
+      btv[k] = i < nspan ? bt[first_blk + i] : -1;
+    }
   }
 
   // Query operand (B of the score products): head column `col`, dims
@@ -146,6 +135,34 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_mfma_kernel(RowAttnArgs a)
       qB[kc] = __builtin_bit_cast(bf16x8m, v);
     }
   }
+
+  const int L = min(a.context_lens[row], a.max_context);
+  if (L <= 0) {  // violated precondition: define the output as zeros
+    if (p == 0)
+      for (int idx = threadIdx.x; idx < HG * D; idx += 64 * NW)
+        out[((long)row * a.num_q_heads + h0) * D + idx] = 0;
+    return;
+  }
+  const int nparts = num_parts(L, a.part_tokens);
+  if (p >= nparts) return;
+  const int part_end = min(L, part_begin + a.part_tokens);
+  // This wave's quarter of the partition (possibly empty).
+  const int quarter = a.part_tokens / NW;
+  const int tok_begin = part_begin + wv * quarter;
+  const int tok_end = min(part_end, tok_begin + quarter);
+
+  // The partition's block IDs, clamped into the pool; each wave's V staging
+  // rows; the quarters' states for the merge.
+  __shared__ int s_bt[kDecodePartition];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vall[NW][CH * RS];
+  __shared__ float s_state[NW - 1][D / 4 + 2][64];
+  uint16_t* s_v = s_vall[wv];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int i = (int)threadIdx.x + k * 64 * NW;
+    if (i < kDecodePartition) s_bt[i] = clamp_block(btv[k], nb);
+  }
+  __syncthreads();
 
   const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
