@@ -75,13 +75,12 @@ __device__ __forceinline__ u32x4 stream_rsrc(const void* base, unsigned bytes) {
 }
 
 // 16 bytes per lane from buffer offset voff straight into LDS: the wave's 64
-// lanes fill 1 KiB at dst (wave-uniform) in lane order; NT adds the
-// non-temporal cache policy (gfx940-family bit NT).  Issued as inline
-// assembly so that the compiler does not add its own waits for it; the
-// caller orders it with vm_wait and barriers.
+// lanes fill 1 KiB at LDS byte address `lds` (wave-uniform) in lane order;
+// NT adds the non-temporal cache policy (gfx940-family bit NT).  Issued as
+// inline assembly so that the compiler does not add its own waits for it;
+// the caller orders it with vm_wait and barriers.
 template <bool NT>
-__device__ __forceinline__ void lds_load16(u32x4 rsrc, uint16_t* dst, unsigned voff) {
-  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
+__device__ __forceinline__ void lds_load16(u32x4 rsrc, unsigned lds, unsigned voff) {
   if constexpr (NT)
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :
@@ -363,6 +362,15 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   const int bs = a.block_size;
   const int bs_log2 = a.block_size_log2;
   const int nblk = a.num_blocks;
+  // Byte addresses of this KV head's rows in the pools, and the bytes from
+  // one block to the next: a tile's descriptor base is then one product and
+  // two additions away.
+  const char* khead = reinterpret_cast<const char*>(a.k_cache) + (long)g * D * 2;
+  const char* vhead = reinterpret_cast<const char*>(a.v_cache) + (long)g * D * 2;
+  const unsigned blk_bytes = (unsigned)bs * row_bytes;  // < 2^32 on this path (launcher)
+  // LDS byte address of stage 0 (a constant of the kernel).
+  const unsigned st_lds =
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&st[0][0];
 
   // Load i of this wave fills physical chunks [(w * NI + i) * 64, +64) of a
   // tile: row s / CPR, physical chunk s % CPR, which holds logical chunk
@@ -376,26 +384,30 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
     src_off[i] = (unsigned)r * row_bytes + (unsigned)(c * 16);
   }
 
-  // Request tile kt, which lies in physical block blk_id, into stage buffers
-  // (dk, dv).  Rows past Lk lie outside the descriptors and arrive as zeros.
+  // Request tile kt, which lies in physical block blk_id, into LDS stage
+  // `stage` (K rows, then V rows).  Rows past Lk lie outside the descriptors
+  // and arrive as zeros.
   const bool stream_tiles = POL == kTilesStreamed || (POL == kTilesPerItem && Lq == 1);
-  auto request = [&](uint16_t* dk, uint16_t* dv, int kt, int blk_id) __attribute__((always_inline)) {
+  auto request = [&](int stage, int kt, int blk_id) __attribute__((always_inline)) {
     const int t0 = kt * BN;
     const int blk = clamp_block(blk_id, nblk);
-    const long base = (((long)blk << bs_log2) + (t0 & (bs - 1))) * slot_elems + (long)g * D;
+    const unsigned long long off = (unsigned long long)(unsigned)blk * blk_bytes +
+                                   (unsigned)(t0 & (bs - 1)) * row_bytes;
     const unsigned bytes = (unsigned)min(BN, Lk - t0) * row_bytes;
-    const u32x4 rk = stream_rsrc(kcache + base, bytes);
-    const u32x4 rv = stream_rsrc(vcache + base, bytes);
+    const u32x4 rk = stream_rsrc(khead + off, bytes);
+    const u32x4 rv = stream_rsrc(vhead + off, bytes);
+    const unsigned dk = st_lds + (unsigned)(stage * 2 * BN * D * 2 + w * NI * 1024);
+    const unsigned dv = dk + BN * D * 2;
     if (stream_tiles) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_load16<true>(rk, dk + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<true>(rk, dk + i * 1024, src_off[i]);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_load16<true>(rv, dv + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<true>(rv, dv + i * 1024, src_off[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_load16<false>(rk, dk + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<false>(rk, dk + i * 1024, src_off[i]);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_load16<false>(rv, dv + (w * NI + i) * 512, src_off[i]);
+      for (int i = 0; i < NI; ++i) lds_load16<false>(rv, dv + i * 1024, src_off[i]);
     }
   };
 
@@ -566,7 +578,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if (kt + NST - 1 < n_tiles) {
-        request(nk, nv, kt + NST - 1, blk_next);
+        request((S + NST - 1) % NST, kt + NST - 1, blk_next);
         // The block of the next request is loaded a step ahead, so that the
         // wave never waits on the block table.
         if (kt + NST < n_tiles) blk_next = bt[((kt + NST) * BN) >> bs_log2];
@@ -584,7 +596,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_OCC) void prefill_bf16_kernel(
   for (int t = 0; t < NST - 1; ++t) {
     if (t < n_tiles) {
       if constexpr (DMA) {
-        request(st[t], st[t] + BN * D, t, bt[(t * BN) >> bs_log2]);
+        request(t, t, bt[(t * BN) >> bs_log2]);
       } else {
         fetch(t);
         deposit(st[t], st[t] + BN * D);
@@ -706,7 +718,9 @@ static int launch_hpw(const PrefillArgs& a, hipStream_t stream) {
       n_qt * a.num_seqs * (long long)a.num_kv_heads * (a.group / HPW);
   if (n_items <= 0) return 0;
   if (n_items > 0x7fffffffLL) return -1;
-  if (a.block_size_log2 >= 0 && (1 << a.block_size_log2) >= PA_PREFILL_BN) {
+  const long long row_bytes = (long long)a.num_kv_heads * D * 2;
+  if (a.block_size_log2 >= 0 && (1 << a.block_size_log2) >= PA_PREFILL_BN &&
+      (1LL << a.block_size_log2) * row_bytes < (1LL << 32)) {
     // Tiles inside one block.  When every query row is a decode row (one
     // row per sequence), each key/value tile is read by a single item:
     // those launches stream the tiles past the caches, as decode does; any
