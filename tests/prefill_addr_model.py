@@ -76,7 +76,10 @@ class Geometry:
 
     @property
     def dma(self) -> bool:
-        return self.bs_log2 >= 0 and self.block_size >= BN
+        # Direct-to-LDS tiles need whole tiles inside a block, and the kernel
+        # keeps a block's byte stride in 32 bits.
+        return (self.bs_log2 >= 0 and self.block_size >= BN and
+                self.block_size * self.row_bytes < (1 << 32))
 
     @property
     def row_bytes(self) -> int:
@@ -163,6 +166,16 @@ def tile_request(geo: Geometry, b: int, g: int, kt: int, bd: Bounds) -> Tuple[in
     if off + rows > geo.block_size:
         raise AddressError(f"tile {kt} of sequence {b} leaves its block")
     lo = ((blk * geo.block_size + off) * geo.num_kv_heads + g) * geo.head_dim * ELEM
+    # The kernel's form of the same base: the head's row in the pool, plus
+    # block x (32-bit block stride) and row-in-block x row bytes, both
+    # products in unsigned 32-bit arithmetic.
+    blk_bytes = geo.block_size * geo.row_bytes
+    in_blk = off * geo.row_bytes
+    if not (blk_bytes < (1 << 32) and in_blk < (1 << 32)):
+        raise AddressError(f"32-bit stride overflow (block bytes {blk_bytes}, row offset {in_blk})")
+    kernel_lo = g * geo.head_dim * ELEM + blk * blk_bytes + in_blk
+    if kernel_lo != lo:
+        raise AddressError(f"descriptor base {kernel_lo} differs from the slot formula's {lo}")
     hi = lo + (rows - 1) * geo.row_bytes + geo.head_dim * ELEM
     return lo, hi
 
@@ -186,7 +199,8 @@ def gathered_rows(geo: Geometry, b: int, g: int, kt: int, bd: Bounds) -> Tuple[i
 
 def check_lds_layout(geo: Geometry) -> None:
     """Every wave's 1 KiB request slices tile their stage's K (then V) half
-    exactly."""
+    exactly; the LDS byte addresses the kernel hands the loads (stage base +
+    wave slice, V half after the K half) cover the NST stages once."""
     cpr = geo.head_dim // 8
     ni = BN * cpr // 256
     half = BN * geo.head_dim
@@ -197,6 +211,19 @@ def check_lds_layout(geo: Geometry) -> None:
             if lo < 0 or lo + 512 > half:
                 raise AddressError(f"LDS slice {lo} of wave {w} outside the stage half")
             covered[lo:lo + 512] += 1
+    stage_bytes = 2 * half * ELEM
+    lds = np.zeros(NST * stage_bytes, np.int32)
+    for stage in range(NST):
+        for w in range(WAVES):
+            dk = stage * stage_bytes + w * ni * 1024
+            dv = dk + half * ELEM
+            for i in range(ni):
+                for a in (dk + i * 1024, dv + i * 1024):
+                    if a < 0 or a + 1024 > lds.size:
+                        raise AddressError(f"LDS byte address {a} outside the stages")
+                    lds[a:a + 1024] += 1
+    if not np.all(lds == 1):
+        raise AddressError("LDS byte addresses do not cover the stages exactly once")
     if not np.all(covered == 1):
         raise AddressError("the request slices do not tile the stage half exactly")
 

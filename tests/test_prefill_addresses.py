@@ -151,3 +151,13 @@ def test_guarded_block_reads_on_workloads(config):
     # at block 256 the first three tiles always sit in block 0: the early
     # order reads nothing stray on these workloads
     assert _stray(geo, m.early_block_reads) == []
+
+
+def test_direct_to_lds_path_needs_a_32_bit_block_stride():
+    """Block sizes whose byte stride would not fit in 32 bits take the
+    register loader (the launcher's test, restated by the model)."""
+    z = np.zeros(2, np.int64)
+    t = np.zeros((1, 1), np.int64)
+    ok = m.Geometry(16, 8, 128, 1 << 20, 1, 1, 1, 1, 1, z, z, t)   # 2 GiB per block
+    big = m.Geometry(16, 8, 128, 1 << 21, 1, 1, 1, 1, 1, z, z, t)  # 4 GiB per block
+    assert ok.dma and not big.dma
