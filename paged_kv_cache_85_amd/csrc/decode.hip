@@ -891,11 +891,9 @@ done:
 // a common max and normalise.  Lane p holds partition p's (max, sum); each
 // lane owns D / 64 output elements.  The sums run over the partitions in
 // order, so the result does not depend on which wave folded which partition.
-// The row length, the first 64 partitions' (max, sum) and the first kPre
-// partitions' partial rows are requested together, before the length is
-// known (every index stays inside the row's max_parts workspace entries;
-// values past the row's partitions are never used), so that one memory
-// latency, not three, precedes the arithmetic.
+// The row length comes first (the partition kernel has just read it, so it
+// is an L2 hit); then the row's own partitions only -- the first 64 (max,
+// sum) pairs and the first kPre partial rows -- are requested together.
 constexpr int kCombinePre = 8;
 
 template <typename E, int D>
@@ -907,18 +905,16 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   const int lane = threadIdx.x;
   const float* ml = a.ws_ml + oh * a.max_parts * 2;
   const float* po = a.ws_o + oh * a.max_parts * D + lane * PER;
-  const int Lraw = a.context_lens[row];
+  const int L = min(a.context_lens[row], a.max_context);
+  const int nparts = num_parts(L, a.part_tokens);
+  if (nparts <= 1) return;
   float2 ml0 = make_float2(kNegBig, 0.f);
-  if (lane < a.max_parts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
+  if (lane < nparts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
   float pre[kCombinePre][PER];
 #pragma unroll
   for (int j = 0; j < kCombinePre; ++j)
 #pragma unroll
-    for (int e = 0; e < PER; ++e) pre[j][e] = j < a.max_parts ? po[(long)j * D + e] : 0.f;
-
-  const int L = min(Lraw, a.max_context);
-  const int nparts = num_parts(L, a.part_tokens);
-  if (nparts <= 1) return;
+    for (int e = 0; e < PER; ++e) pre[j][e] = j < nparts ? po[(long)j * D + e] : 0.f;
   float M = kNegBig;
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     float mx = p0 + lane < nparts ? (p0 == 0 ? ml0.x : ml[2 * (p0 + lane)]) : kNegBig;
