@@ -164,3 +164,39 @@ def test_prefill_empty_is_noop():
     bt = torch.zeros((2, 1), dtype=torch.int32, device="cuda:0")
     cu = torch.zeros((3,), dtype=torch.int32, device="cuda:0")
     pa.pa_prefill_varlen(z, z, pool, pool, bt, cu, cu, 0, 0, 0.125)
+
+
+def test_prefill_block_stride_past_32_bits_matches_small_blocks():
+    """A 4 GiB block (2^24 rows of 2 heads x 64 bf16) has a byte stride that
+    the direct-to-LDS loads do not hold in 32 bits, so the call gathers its
+    tiles row by row; the output equals that of a pool of 256-token blocks bit
+    for bit (both loaders fill the same LDS layout)."""
+    import math
+
+    import torch
+
+    import paged_kv_cache_85_amd as pa
+    rng = np.random.default_rng(11)
+    L, hq, hkv, d = 150, 4, 2, 64
+
+    def bf(shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(
+            torch.bfloat16).to("cuda:0")
+
+    q, k, v = bf((L, hq, d)), bf((L, hkv, d)), bf((L, hkv, d))
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda:0")
+    bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda:0")
+    slots = torch.arange(L, dtype=torch.int32, device="cuda:0")
+    outs = []
+    for bs in (256, 1 << 24):
+        say(f"block_size {bs}: pools of {bs * hkv * d * 2 / 2**30:.3g} GiB each")
+        kc = torch.empty((1, bs, hkv, d), dtype=torch.bfloat16, device="cuda:0")
+        vc = torch.empty_like(kc)
+        pa.pa_store_kv(k, v, kc, vc, slots)
+        out = torch.empty_like(q)
+        pa.pa_prefill_varlen(out, q, kc, vc, bt, cu, cu, L, L, 1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        outs.append(bits(out))
+        del kc, vc
+        torch.cuda.empty_cache()
+    assert np.array_equal(outs[0], outs[1])
