@@ -267,3 +267,40 @@ def test_decode_empty_batch_is_noop():
     bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda:0")
     cl = torch.zeros((0,), dtype=torch.int32, device="cuda:0")
     pa.pa_decode(z, z, pool, pool, bt, cl, 1, 0.125)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2)])
+def test_decode_block_stride_past_32_bits_matches_small_blocks(hq, hkv):
+    """4 GiB blocks (2^24 rows of 2 heads x 64 bf16: a byte stride past 32
+    bits) give the same decode output, bit for bit, as 256-token blocks --
+    on the vector fold (group 2) and on the matrix cores (group 8), for a row
+    of two partitions."""
+    import math
+
+    import torch
+
+    import paged_kv_cache_85_amd as pa
+    rng = np.random.default_rng(13)
+    L, d = 700, 64
+
+    def bf(shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(
+            torch.bfloat16).to("cuda:0")
+
+    q, k, v = bf((1, hq, d)), bf((L, hkv, d)), bf((L, hkv, d))
+    slots = torch.arange(L, dtype=torch.int32, device="cuda:0")
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda:0")
+    outs = []
+    for bs, nblk in ((256, 3), (1 << 24, 1)):
+        say(f"hq {hq} hkv {hkv} block_size {bs}")
+        kc = torch.empty((nblk, bs, hkv, d), dtype=torch.bfloat16, device="cuda:0")
+        vc = torch.empty_like(kc)
+        bt = torch.arange(nblk, dtype=torch.int32, device="cuda:0").view(1, nblk)
+        pa.pa_store_kv(k, v, kc, vc, slots)
+        out = torch.empty_like(q)
+        pa.pa_decode(out, q, kc, vc, bt, lens, L, 1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        outs.append(bits(out))
+        del kc, vc
+        torch.cuda.empty_cache()
+    assert np.array_equal(outs[0], outs[1])
