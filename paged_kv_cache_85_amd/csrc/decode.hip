@@ -4,9 +4,9 @@
 // A decode step scores one new query row per sequence against the whole
 // stored history of that sequence ("mini-vLLM", project summary), read
 // through the sequence's block table ("nano-vLLM Part 4", section 3: decode
-// attention over the cached history).  The work is HBM-bound (about 2 FLOP per byte of
-// bf16 KV at a query group of 2), so the kernels are organised around the
-// memory stream, not the matrix cores:
+// attention over the cached history).  The work is HBM-bound (about 2 FLOP
+// per byte of bf16 KV at a query group of 2), so the kernels are organised
+// around the memory stream, not the matrix cores:
 //
 //  * the unit of work is an item = (sequence, 512-token context partition,
 //    KV head); the query heads of the KV head's group (up to HG of them)
