@@ -891,9 +891,12 @@ done:
 // a common max and normalise.  Lane p holds partition p's (max, sum); each
 // lane owns D / 64 output elements.  The sums run over the partitions in
 // order, so the result does not depend on which wave folded which partition.
-// The row length comes first (the partition kernel has just read it, so it
-// is an L2 hit); then the row's own partitions only -- the first 64 (max,
-// sum) pairs and the first kPre partial rows -- are requested together.
+// The row length, the first 64 partitions' (max, sum) pairs and the partial
+// rows of partitions 0 and 1 (every row that needs a combine has both) are
+// requested together; the partial rows of partitions 2 .. kPre - 1 follow
+// once the length shows that the row has them.  So a two-partition row
+// waits for one memory latency, and no partial row is read that the row
+// does not have (indices stay inside the row's max_parts workspace entries).
 constexpr int kCombinePre = 8;
 
 template <typename E, int D>
@@ -905,14 +908,19 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(RowAttnArgs a) {
   const int lane = threadIdx.x;
   const float* ml = a.ws_ml + oh * a.max_parts * 2;
   const float* po = a.ws_o + oh * a.max_parts * D + lane * PER;
-  const int L = min(a.context_lens[row], a.max_context);
-  const int nparts = num_parts(L, a.part_tokens);
-  if (nparts <= 1) return;
+  const int Lraw = a.context_lens[row];
   float2 ml0 = make_float2(kNegBig, 0.f);
-  if (lane < nparts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
+  if (lane < a.max_parts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
   float pre[kCombinePre][PER];
 #pragma unroll
-  for (int j = 0; j < kCombinePre; ++j)
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[j][e] = po[(long)j * D + e];   // max_parts >= 2 here
+  const int L = min(Lraw, a.max_context);
+  const int nparts = num_parts(L, a.part_tokens);
+  if (nparts <= 1) return;
+#pragma unroll
+  for (int j = 2; j < kCombinePre; ++j)
 #pragma unroll
     for (int e = 0; e < PER; ++e) pre[j][e] = j < nparts ? po[(long)j * D + e] : 0.f;
   float M = kNegBig;
