@@ -304,3 +304,15 @@ def test_decode_block_stride_past_32_bits_matches_small_blocks(hq, hkv):
         del kc, vc
         torch.cuda.empty_cache()
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2)])
+def test_decode_more_than_64_partitions(hq, hkv):
+    """A 40,000-token row has 79 partitions: the combine kernel merges them
+    in two chunks of up to 64 (max, sum) pairs, beyond its eight prefetched
+    partial rows.  Vector fold (group 2) and matrix cores (group 8)."""
+    spec = DecodeSpec(f"dec-79-parts-{hq}", hq, hkv, 64, "bf16", 256,
+                      context_lens=(40000, 3, 513, 33000))
+    case = make_decode(spec, 29)
+    out, _, _ = run_decode(case)
+    assert_close(f64(out), _oracle(case), "bf16", spec.name)
