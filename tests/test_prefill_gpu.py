@@ -200,3 +200,28 @@ def test_prefill_block_stride_past_32_bits_matches_small_blocks():
         del kc, vc
         torch.cuda.empty_cache()
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("bs", [256, 16])
+def test_prefill_long_prompts_sampled(bs):
+    """Long items: a 12,000-token prompt (375 key tiles for its last query
+    tile), a 3,000-token one and a short one behind a 500-token cached
+    prefix.  The whole call runs on the GPU; 96 sampled rows are checked
+    against the oracle, each as attention over its own visible keys."""
+    spec = PrefillSpec(f"pre-long-{bs}", 8, 4, 128, "bf16", bs, q_len_range=(1, 1),
+                       q_lens=(12000, 37, 3000), prefix_lens=(0, 500, 0))
+    case = make_prefill(spec, 61)
+    out, _, _ = run_prefill(case)
+    out = f64(out)
+    kc, vc = oracle.store_kv(case.k_cache, case.v_cache, case.k_new, case.v_new,
+                             case.slot_mapping)
+    rng = np.random.default_rng(5)
+    for b in range(case.num_seqs):
+        q0, q1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
+        lk = int(case.cu_seqlens_k[b + 1] - case.cu_seqlens_k[b])
+        lq = q1 - q0
+        rows = np.unique(np.concatenate([[0, lq - 1], rng.integers(0, lq, 30)]))
+        lens = np.asarray([lk - lq + i + 1 for i in rows], np.int32)
+        bt = np.repeat(case.block_tables[b:b + 1], len(rows), axis=0)
+        ref = oracle.decode(case.q[q0 + rows], kc, vc, bt, lens, case.scale, case.dtype)
+        assert_close(out[q0 + rows], ref, "bf16", f"{spec.name} sequence {b}")
